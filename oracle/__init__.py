@@ -1,0 +1,19 @@
+"""fp64 CPU oracle for exact attention -- test infrastructure only.
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+import this package.  The library never does.
+"""
+
+from .exact_attention import (  # noqa: F401
+    attention_head,
+    attention_ref,
+    attention_rows,
+    finalize,
+    merge_stats,
+    partial_stats,
+    probabilities,
+    scores,
+    softmax_stats,
+    tiled_online_attention,
+    visible,
+)

@@ -1,0 +1,263 @@
+"""Plain, slow fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the package smoke check and the CPU
+baseline leg of the benchmark use it.  It shares no code, tables or helpers
+with the HIP kernels and imports nothing from the library package.
+
+What it computes (the plain definition, written out):
+
+    S_ij   = scale * sum_k q_ik * k_jk                  (full score rows)
+    A_ij   = True if non-causal, else (j <= i)          (causal mask)
+    m_i    = max_{j: A_ij} S_ij
+    P_ij   = exp(S_ij - m_i) if A_ij else 0
+    l_i    = sum_j P_ij
+    O_i    = (sum_j P_ij * v_j) / l_i
+    LSE_i  = m_i + ln(l_i)
+
+Sources (web pages on FlashAttention-2):
+  * Saraf, "FlashAttention 2: Three Places the Chip Was Still Waiting",
+    section 1 (the naive kernel builds the full token-by-token score matrix;
+    online softmax carries a running max and denominator and gives the exact
+    answer) and section 3 (the tiled kernel's output is identical to standard
+    attention; only the schedule changes).
+  * papermap "FlashAttention-2" explainer, Chapter 02, "What stays true from
+    FA1" (exact attention, identical outputs; the N x N matrix never reaches
+    HBM in the fast kernel).
+  * Mishra, "FlashAttention-2 and -3: From Algebra to GPU Scheduling",
+    "Keep the unchanged mathematical target in view" (running max,
+    denominator and numerator define the output; their merge identity is what
+    makes tiling correct) and "Another use of mergeable statistics".
+
+Readings where the pages are silent (each listed in the design notes):
+  * the scale multiplies the raw dot products before the softmax;
+  * causal means key j is visible to query i iff j <= i (equal lengths);
+  * LSE is the natural log of sum_j exp(S_ij) over visible keys.
+
+Everything here is float64 numpy.  Inputs of any float dtype are upcast
+exactly (bf16 and fp32 values are exactly representable in fp64).
+
+The module also holds the fp64 rendering of the pages' tiled algorithm
+(``tiled_online_attention``), which walks key blocks with a running max and
+denominator in the order the pages describe.  It is not the oracle; tests use
+it to check the pages' exactness claims against the oracle.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "scores",
+    "visible",
+    "softmax_stats",
+    "finalize",
+    "attention_head",
+    "attention_ref",
+    "attention_rows",
+    "probabilities",
+    "partial_stats",
+    "merge_stats",
+    "tiled_online_attention",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --- the definition, one step per function ---------------------------------
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * Q K^T for one head: q [nq, d], k [nk, d] -> [nq, nk].
+
+    Saraf §1: each score compares one query row with one key row.
+    """
+    return float(scale) * (q @ k.T)
+
+
+def visible(row_ids, key_ids, causal: bool) -> np.ndarray:
+    """Boolean mask [len(row_ids), len(key_ids)]; True where query row i may
+    attend to key j.
+
+    Causal reading: key j is visible to query i iff j <= i.
+    """
+    rows = np.asarray(row_ids)[:, None]
+    cols = np.asarray(key_ids)[None, :]
+    if not causal:
+        return np.ones((rows.shape[0], cols.shape[1]), dtype=bool)
+    return cols <= rows
+
+
+def softmax_stats(s: np.ndarray, mask: np.ndarray, v: np.ndarray):
+    """Row statistics over the visible keys of a score block.
+
+    Returns (m, l, num): the row max of visible scores, the denominator
+    sum exp(S - m) and the unnormalised numerator sum exp(S - m) v_j
+    (Mishra, "Keep the unchanged mathematical target in view").
+    Rows with no visible key get m = -inf, l = 0, num = 0.
+    """
+    s_vis = np.where(mask, s, -np.inf)
+    m = s_vis.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    shift = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(np.where(mask, s - shift[:, None], -np.inf))
+    l = p.sum(axis=1)
+    num = p @ v
+    return m, l, num
+
+
+def finalize(m: np.ndarray, l: np.ndarray, num: np.ndarray):
+    """O = num / l and LSE = m + ln l: the single normalisation at the end."""
+    o = num / l[:, None]
+    lse = m + np.log(l)
+    return o, lse
+
+
+def attention_head(q, k, v, scale: float, causal: bool, rows=None, row_block: int = 1024):
+    """Exact attention for one head.
+
+    q, k, v: [N, d] (upcast to fp64).  ``rows`` selects query rows (default:
+    all).  Full score rows are materialised, ``row_block`` query rows at a
+    time; nothing is tiled along the keys.
+    Returns (O [len(rows), d], LSE [len(rows)]) in fp64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = q.shape[0]
+    row_ids = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(row_ids), v.shape[1]), dtype=np.float64)
+    lse = np.empty(len(row_ids), dtype=np.float64)
+    for start in range(0, len(row_ids), row_block):
+        ids = row_ids[start:start + row_block]
+        s = scores(q[ids], k, scale)
+        mask = visible(ids, np.arange(k.shape[0]), causal)
+        m, l, num = softmax_stats(s, mask, v)
+        o[start:start + len(ids)], lse[start:start + len(ids)] = finalize(m, l, num)
+    return o, lse
+
+
+def attention_ref(q, k, v, scale: float, causal: bool, row_block: int = 1024):
+    """Exact attention over [..., N, d] tensors (e.g. [B, H, N, d]).
+
+    Returns (O [..., N, d], LSE [..., N]) as fp64 numpy arrays.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    n, dv = q.shape[-2], v.shape[-1]
+    o = np.empty(lead + (n, dv), dtype=np.float64)
+    lse = np.empty(lead + (n,), dtype=np.float64)
+    for idx in np.ndindex(*lead):
+        o[idx], lse[idx] = attention_head(q[idx], k[idx], v[idx], scale, causal, row_block=row_block)
+    return o, lse
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, rows):
+    """Exact attention for selected query rows of one head (sampled checks)."""
+    return attention_head(q, k, v, scale, causal, rows=rows)
+
+
+def probabilities(q, k, scale: float, causal: bool) -> np.ndarray:
+    """Normalised attention probabilities P / l for one head, [N, N]."""
+    q, k = _f64(q), _f64(k)
+    ids = np.arange(q.shape[0])
+    s = scores(q, k, scale)
+    mask = visible(ids, np.arange(k.shape[0]), causal)
+    s_vis = np.where(mask, s, -np.inf)
+    m = s_vis.max(axis=1)
+    p = np.exp(np.where(mask, s - m[:, None], -np.inf))
+    return p / p.sum(axis=1, keepdims=True)
+
+
+# --- mergeable statistics ---------------------------------------------------
+
+def partial_stats(q, k, v, scale: float, causal: bool, key_ids):
+    """(m, l, num) of every query row of one head over a subset of the keys.
+
+    Mishra, "Keep the unchanged mathematical target in view" and "Another use
+    of mergeable statistics": statistics of disjoint key sets can be combined
+    exactly.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    key_ids = np.asarray(key_ids, dtype=np.int64)
+    ids = np.arange(q.shape[0])
+    s = scores(q, k[key_ids], scale)
+    mask = visible(ids, key_ids, causal)
+    return softmax_stats(s, mask, v[key_ids])
+
+
+def merge_stats(parts):
+    """Combine (m, l, num) of disjoint key sets into the statistics of their union.
+
+    m = max_a m_a; each part is brought onto the common max by exp(m_a - m)
+    before its denominator and numerator are added.
+    """
+    ms = np.stack([p[0] for p in parts])
+    m = ms.max(axis=0)
+    shift = np.where(np.isfinite(m), m, 0.0)
+    l = np.zeros_like(parts[0][1])
+    num = np.zeros_like(parts[0][2])
+    for pm, pl, pnum in parts:
+        w = np.where(np.isfinite(pm), np.exp(np.where(np.isfinite(pm), pm, 0.0) - shift), 0.0)
+        l = l + w * pl
+        num = num + w[:, None] * pnum
+    return m, l, num
+
+
+# --- the pages' tiled schedule, in fp64 (for checking the exactness claims) --
+
+def tiled_online_attention(q, k, v, scale: float, causal: bool, block_rows: int = 64,
+                           block_cols: int = 64, normalize_each_step: bool = False):
+    """The tiled online-softmax algorithm of the pages, in fp64, for one head.
+
+    Query rows are taken ``block_rows`` at a time (Saraf §2.3: independent
+    query blocks).  Each block streams the key/value blocks past itself,
+    keeping a running max m, denominator l and accumulator acc per row
+    (Saraf §1).  When the running max rises, the banked terms are corrected
+    by exp(m_old - m_new) (Saraf §2.2, the correction that cannot wait).
+
+    normalize_each_step=False: acc stays unnormalised and is divided by l once
+    per query block (the FlashAttention-2 schedule, Saraf §2.2).
+    normalize_each_step=True: acc always holds the normalised output and is
+    rescaled by l_old / l_new every step (the FlashAttention-1 schedule the
+    same section describes).
+
+    Returns (O [N, d], LSE [N], normalisations) where ``normalisations`` counts
+    how often an accumulator block was divided.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, nk = q.shape[0], k.shape[0]
+    o = np.empty((n, v.shape[1]))
+    lse = np.empty(n)
+    normalisations = 0
+    for r0 in range(0, n, block_rows):
+        ids = np.arange(r0, min(r0 + block_rows, n))
+        m = np.full(len(ids), -np.inf)
+        l = np.zeros(len(ids))
+        acc = np.zeros((len(ids), v.shape[1]))
+        for c0 in range(0, nk, block_cols):
+            kids = np.arange(c0, min(c0 + block_cols, nk))
+            mask = visible(ids, kids, causal)
+            if not mask.any():
+                continue
+            s = scores(q[ids], k[kids], scale)
+            s_vis = np.where(mask, s, -np.inf)
+            m_new = np.maximum(m, s_vis.max(axis=1))
+            shift = np.where(np.isfinite(m_new), m_new, 0.0)
+            corr = np.where(np.isfinite(m), np.exp(np.where(np.isfinite(m), m, 0.0) - shift), 0.0)
+            p = np.exp(np.where(mask, s - shift[:, None], -np.inf))
+            l_new = corr * l + p.sum(axis=1)
+            if normalize_each_step:
+                # acc holds O normalised by l; bring it to the new max and the
+                # new denominator, then add this block's normalised share.
+                keep = np.where(l_new > 0, corr * l / np.where(l_new > 0, l_new, 1.0), 0.0)
+                acc = keep[:, None] * acc + (p @ v[kids]) / np.where(l_new > 0, l_new, 1.0)[:, None]
+                normalisations += 1
+            else:
+                acc = corr[:, None] * acc + p @ v[kids]
+            m, l = m_new, l_new
+        if normalize_each_step:
+            o[ids] = acc
+        else:
+            o[ids] = acc / l[:, None]
+            normalisations += 1
+        lse[ids] = m + np.log(l)
+    return o, lse, normalisations

@@ -1,0 +1,86 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Every mutant replaces one step function of ``oracle.attention_ref`` (on the
+CPU, for the duration of one test) with a plausibly wrong version: a
+dropped term, a wrong sign or index, a transposed operand, a wrong mask.
+The test passes only if the pin suite catches it -- evidence that the pins
+constrain every step of the oracle, not just that the oracle agrees with
+itself.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.exact_attention as ref
+from oracle_pins import PINS
+
+_orig_scores = ref.scores
+_orig_visible = ref.visible
+_orig_stats = ref.softmax_stats
+_orig_finalize = ref.finalize
+
+
+def _stats_no_shift(s, mask, v):
+    p = np.where(mask, np.exp(s), 0.0)
+    m = np.zeros(s.shape[0])
+    return m, p.sum(axis=1), p @ v
+
+
+def _stats_mask_ignored_in_l(s, mask, v):
+    m, _, num = _orig_stats(s, mask, v)
+    l = np.exp(s - np.where(np.isfinite(m), m, 0.0)[:, None]).sum(axis=1)
+    return m, l, num
+
+
+def _stats_exp2(s, mask, v):
+    s_vis = np.where(mask, s, -np.inf)
+    m = s_vis.max(axis=1)
+    p = np.where(mask, np.exp2(s - m[:, None]), 0.0)
+    return m, p.sum(axis=1), p @ v
+
+
+def _stats_reversed_v(s, mask, v):
+    return _orig_stats(s, mask, v[::-1])
+
+
+def _stats_m_from_all_keys(s, mask, v):
+    m = s.max(axis=1)
+    p = np.where(mask, np.exp(s - m[:, None]), 0.0)
+    return m, p.sum(axis=1), p @ v
+
+
+MUTANTS = {
+    "scores_transposed": ("scores", lambda q, k, scale: float(scale) * (k @ q.T)
+                          if q.shape == k.shape else float(scale) * (q @ k.T) + 1.0),
+    "scores_scale_dropped": ("scores", lambda q, k, scale: q @ k.T),
+    "scores_scale_squared": ("scores", lambda q, k, scale: float(scale) ** 2 * (q @ k.T)),
+    "scores_sign_flipped": ("scores", lambda q, k, scale: -float(scale) * (q @ k.T)),
+    "mask_reversed": ("visible", lambda r, c, causal: _orig_visible(r, c, False) if not causal
+                      else np.asarray(c)[None, :] >= np.asarray(r)[:, None]),
+    "mask_strict": ("visible", lambda r, c, causal: _orig_visible(r, c, False) if not causal
+                    else np.asarray(c)[None, :] < np.asarray(r)[:, None]),
+    "mask_ignored": ("visible", lambda r, c, causal: _orig_visible(r, c, False)),
+    "stats_no_max_shift": ("softmax_stats", _stats_no_shift),
+    "stats_l_counts_masked": ("softmax_stats", _stats_mask_ignored_in_l),
+    "stats_exp2_for_exp": ("softmax_stats", _stats_exp2),
+    "stats_reversed_v": ("softmax_stats", _stats_reversed_v),
+    "stats_max_over_masked": ("softmax_stats", _stats_m_from_all_keys),
+    "finalize_lse_without_m": ("finalize", lambda m, l, num: (num / l[:, None], np.log(l))),
+    "finalize_lse_sign": ("finalize", lambda m, l, num: (num / l[:, None], m - np.log(l))),
+    "finalize_unnormalised": ("finalize", lambda m, l, num: (num, m + np.log(l))),
+    "finalize_log2": ("finalize", lambda m, l, num: (num / l[:, None], m + np.log2(l))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name!r} passed every pin"

@@ -1,0 +1,109 @@
+"""Seeded synthetic attention workloads.
+
+This module only describes shapes and draws random inputs.  It holds none of
+the attention arithmetic, so both the fp64 oracle's tests and the GPU path's
+tests and benchmark can use it without sharing any of the method's code.
+
+The five workloads are the pages' own examples of FlashAttention-2 regimes:
+  * fp32_small    -- a tiny fp32 correctness case;
+  * short_seq     -- many short sequences (the explainer's Legacy section notes
+                     gains shrink there; bandwidth-leaning);
+  * mid_seq       -- a mid-length, non-causal case;
+  * long_causal   -- 2 sequences x 16 heads x 8192 tokens, Saraf §2.3's
+                     example, causal, with 0.1% of Q and K entries scaled x20
+                     so the running max has to be corrected;
+  * long_few_head -- 1 x 2 heads x 32768 tokens, the explainer's
+                     "few heads, long sequence" occupancy case.
+
+Recipe (the same for every workload):
+  1. one CPU ``torch.Generator`` seeded with ``seed``;
+  2. Q, K, V drawn in that order as float32 N(0, 1), shape [B, H, N, d];
+  3. if ``outlier_frac`` > 0: independent Bernoulli(outlier_frac) masks for
+     Q then K (from the same generator, uniform < frac); masked entries are
+     multiplied by ``outlier_mult`` in float32 (V untouched);
+  4. cast to the workload dtype (bf16 uses round-to-nearest-even).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "HEADLINE", "make_inputs", "credited_flops", "get"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "fp32" or "bf16"
+    scale: float
+    causal: bool
+    outlier_frac: float = 0.0
+    outlier_mult: float = 1.0
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "fp32" else torch.bfloat16
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    def describe(self) -> dict:
+        return {
+            "workload": self.name,
+            "B": self.B, "H": self.H, "N": self.N, "d": self.d,
+            "dtype": self.dtype, "causal": self.causal, "scale": self.scale,
+            "outlier_frac": self.outlier_frac, "outlier_mult": self.outlier_mult,
+        }
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("fp32_small", 1, 1, 128, 64, "fp32", 1.0 / math.sqrt(64), False),
+        Workload("short_seq", 32, 16, 512, 64, "bf16", 1.0 / 8.0, False),
+        Workload("mid_seq", 8, 16, 2048, 128, "bf16", 1.0 / math.sqrt(128), False),
+        Workload("long_causal", 2, 16, 8192, 128, "bf16", 1.0 / math.sqrt(128), True, 0.001, 20.0),
+        Workload("long_few_head", 1, 2, 32768, 128, "bf16", 1.0 / math.sqrt(128), True),
+    ]
+}
+
+# The workload the headline throughput is quoted on (d=128, N=8192, causal).
+HEADLINE = "long_causal"
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def make_inputs(w: Workload, seed: int, device="cpu"):
+    """Draw (q, k, v) for workload ``w`` with ``seed``; returns tensors on ``device``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = w.shape
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.outlier_frac > 0.0:
+        mq = torch.rand(shape, generator=g) < w.outlier_frac
+        mk = torch.rand(shape, generator=g) < w.outlier_frac
+        q = torch.where(mq, q * w.outlier_mult, q)
+        k = torch.where(mk, k * w.outlier_mult, k)
+    dt = w.torch_dtype
+    return (q.to(dt).to(device), k.to(dt).to(device), v.to(dt).to(device))
+
+
+def credited_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Credited attention-forward work: 4*B*H*N^2*d, halved when causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2.0 if causal else f
