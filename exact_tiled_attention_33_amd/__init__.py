@@ -1,0 +1,171 @@
+"""MI355X (gfx950) FlashAttention-2 forward: a thin ctypes binding of libfa2.so.
+
+The library (``libfa2.so``, built in-tree by ``build_lib``) exports the C ABI
+declared in ``include/fa2.h``.  This module only marshals arguments: every
+step of the computation runs in the library's HIP kernels.  There is no CPU
+fallback -- if the library is missing, every call raises.
+
+Raw entry points (same names and argument order as the C ABI):
+    fa2_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, in_dtype, o_dtype) -> int
+    fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict
+    fa2_strerror(status) -> str
+    fa2_version() -> int
+Convenience wrapper over torch device tensors:
+    forward(q, k, v, causal=False, scale=None, o_dtype=torch.float32) -> (o, lse)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+__all__ = [
+    "F32", "BF16",
+    "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
+    "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
+    "forward", "EXPORTED_SYMBOLS",
+]
+
+F32 = 0
+BF16 = 1
+
+FA2_OK = 0
+FA2_ERR_INVALID_ARG = -1
+FA2_ERR_UNSUPPORTED = -2
+FA2_ERR_NO_DEVICE = -3
+FA2_ERR_LAUNCH = -4
+
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version")
+
+_LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
+_lib = None
+
+
+class Fa2Error(RuntimeError):
+    def __init__(self, status: int, where: str = "fa2_fwd"):
+        self.status = status
+        super().__init__(f"{where} failed with status {status}: {fa2_strerror(status)}")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [
+        ("block_rows", ctypes.c_int),
+        ("block_cols", ctypes.c_int),
+        ("waves_per_group", ctypes.c_int),
+        ("query_tiles", ctypes.c_int),
+        ("workgroups", ctypes.c_longlong),
+        ("tile_pairs", ctypes.c_longlong),
+        ("normalisations", ctypes.c_longlong),
+        ("waves_of_groups", ctypes.c_double),
+        ("last_wave_groups", ctypes.c_int),
+        ("flops_executed", ctypes.c_double),
+        ("flops_credited", ctypes.c_double),
+    ]
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load():
+    """Load libfa2.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it first with "
+            "`python -m exact_tiled_attention_33_amd.build_lib` (or __graft_entry__.build())"
+        )
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    lib.fa2_fwd.restype = ctypes.c_int
+    lib.fa2_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+    ]
+    lib.fa2_plan.restype = ctypes.c_int
+    lib.fa2_plan.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_Plan),
+    ]
+    lib.fa2_strerror.restype = ctypes.c_char_p
+    lib.fa2_strerror.argtypes = [ctypes.c_int]
+    lib.fa2_version.restype = ctypes.c_int
+    lib.fa2_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def fa2_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, in_dtype, o_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale),
+                              stream, in_dtype, o_dtype))
+
+
+def fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict:
+    out = _Plan()
+    st = int(load().fa2_plan(B, H, N, d, int(causal), in_dtype, block_rows, block_cols,
+                             num_units, ctypes.byref(out)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_plan")
+    return {name: getattr(out, name) for name, _ in _Plan._fields_}
+
+
+def fa2_strerror(status: int) -> str:
+    return load().fa2_strerror(int(status)).decode()
+
+
+def fa2_version() -> int:
+    return int(load().fa2_version())
+
+
+def _dtype_code(dt) -> int:
+    import torch
+
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {dt} (bf16 or fp32)")
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=None,
+            out=None, lse=None, stream=None):
+    """Attention forward on [B, H, N, d] device tensors; returns (o, lse).
+
+    ``o_dtype`` defaults to float32.  ``out``/``lse`` may be given to reuse
+    buffers.  The kernels are enqueued on ``stream`` (default: torch's
+    current stream) and this returns without synchronising.
+    """
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {q.shape}, {k.shape}, {v.shape}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of o_dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                 B, H, N, d, causal, scale, handle, _dtype_code(q.dtype), _dtype_code(o_dtype))
+    if st != FA2_OK:
+        raise Fa2Error(st)
+    return out, lse

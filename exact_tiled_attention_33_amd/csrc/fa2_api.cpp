@@ -1,0 +1,137 @@
+// C-ABI front end: argument validation, launch geometry, dispatch.
+//
+// Every check runs before the first HIP call, so malformed calls are
+// rejected identically on machines with and without a GPU.
+
+#include "fa2.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "fa2_launch.h"
+
+namespace {
+
+bool is_dtype(int x) { return x == FA2_F32 || x == FA2_BF16; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [p, p + n) and [q, q + m) share a byte?
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+int check_sizes(int B, int H, int N, int d, int in_dtype) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA2_ERR_INVALID_ARG;
+  if (!is_dtype(in_dtype)) return FA2_ERR_INVALID_ARG;
+  // B*H*N*d elements (and bytes) must fit comfortably in 64-bit offsets.
+  const long double elems = (long double)B * H * N * d;
+  if (elems > (long double)(1LL << 60)) return FA2_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  return FA2_OK;
+}
+
+void own_tiles(int in_dtype, int* rows, int* cols, int* waves) {
+  if (in_dtype == FA2_BF16) {
+    *rows = fa2::kBf16BlockRows; *cols = fa2::kBf16BlockCols; *waves = fa2::kBf16Waves;
+  } else {
+    *rows = fa2::kF32BlockRows; *cols = fa2::kF32BlockCols; *waves = fa2::kF32Waves;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa2_version(void) { return FA2_VERSION; }
+
+const char* fa2_strerror(int status) {
+  switch (status) {
+    case FA2_OK: return "success";
+    case FA2_ERR_INVALID_ARG: return "invalid argument (null/misaligned/overlapping pointer, bad size, scale or dtype code)";
+    case FA2_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128)";
+    case FA2_ERR_NO_DEVICE: return "no HIP device available";
+    case FA2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa2_plan(int B, int H, int N, int d, int causal, int in_dtype, int block_rows, int block_cols,
+             int num_units, fa2_plan_t* out) {
+  if (out == nullptr) return FA2_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  if (block_rows < 0 || block_cols < 0 || num_units < 0) return FA2_ERR_INVALID_ARG;
+  const int st = check_sizes(B, H, N, d, in_dtype);
+  if (st != FA2_OK) return st;
+
+  int br, bc, waves;
+  own_tiles(in_dtype, &br, &bc, &waves);
+  if (block_rows > 0) br = block_rows;
+  if (block_cols > 0) bc = block_cols;
+
+  const long long bh = (long long)B * H;
+  const long long T = (N + (long long)br - 1) / br;
+  const long long nk = (N + (long long)bc - 1) / bc;
+  // Key tiles visited per query tile: all of them, or (causal) those that
+  // start at or below the tile's last row.
+  long long pairs_per_head = 0;
+  for (long long t = 0; t < T; ++t) {
+    if (!causal) {
+      pairs_per_head += nk;
+    } else {
+      const long long last_row = std::min<long long>((t + 1) * br - 1, (long long)N - 1);
+      pairs_per_head += std::min<long long>(nk, last_row / bc + 1);
+    }
+  }
+  out->block_rows = br;
+  out->block_cols = bc;
+  out->waves_per_group = waves;
+  out->query_tiles = (int)T;
+  out->workgroups = bh * T;
+  out->tile_pairs = bh * pairs_per_head;
+  out->normalisations = bh * T;
+  out->waves_of_groups = num_units > 0 ? (double)out->workgroups / num_units : 0.0;
+  out->last_wave_groups = num_units > 0 ? (int)(out->workgroups % num_units) : 0;
+  out->flops_executed = 4.0 * (double)br * bc * d * (double)out->tile_pairs;
+  out->flops_credited = 4.0 * (double)bh * N * (double)N * d / (causal ? 2.0 : 1.0);
+  return FA2_OK;
+}
+
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+            int d, int causal, float scale, void* stream, int in_dtype, int o_dtype) {
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  if (!is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
+  const int st = check_sizes(B, H, N, d, in_dtype);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA2_ERR_INVALID_ARG;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t in_bytes = elems * (in_dtype == FA2_BF16 ? 2 : 4);
+  const size_t o_bytes = elems * (o_dtype == FA2_BF16 ? 2 : 4);
+  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins) {
+    if (overlaps(o, o_bytes, in, in_bytes) || overlaps(lse, lse_bytes, in, in_bytes))
+      return FA2_ERR_INVALID_ARG;
+  }
+  if (overlaps(o, o_bytes, lse, lse_bytes)) return FA2_ERR_INVALID_ARG;
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+
+  fa2::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.o_bf16 = (o_dtype == FA2_BF16);
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = (in_dtype == FA2_BF16) ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // extern "C"

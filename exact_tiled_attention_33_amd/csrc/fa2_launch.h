@@ -1,0 +1,37 @@
+// Internal interface between the C-ABI front end (fa2_api.cpp) and the
+// kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa2 {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  bool causal;
+  float scale;
+  bool o_bf16;
+  hipStream_t stream;
+};
+
+// Tile geometry of each kernel family.  The bf16 kernel gives every
+// wavefront 32 query rows (the N side of a 32x32 MFMA) and streams keys in
+// tiles of kBf16BlockCols; the fp32 kernel does the same with 32-key tiles.
+constexpr int kBf16Waves = 4;
+constexpr int kBf16BlockRows = kBf16Waves * 32;  // 128
+constexpr int kBf16BlockCols = 64;
+constexpr int kF32Waves = 4;
+constexpr int kF32BlockRows = kF32Waves * 32;    // 128
+constexpr int kF32BlockCols = 32;
+
+// Enqueue the forward kernel for bf16 (resp. fp32) inputs.  Arguments are
+// already validated; returns the launch status.
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+
+}  // namespace fa2

@@ -1,0 +1,137 @@
+/*
+ * fa2.h -- C ABI of an MI355X (gfx950) FlashAttention-2 forward pass.
+ *
+ * The operation (exact attention, computed tile by tile with an online
+ * softmax, never writing the N x N score matrix to device memory):
+ *
+ *   S_ij  = scale * <q_i, k_j>
+ *   visible(i, j) = true            (non-causal)
+ *                 = (j <= i)        (causal)
+ *   m_i   = max_{visible j} S_ij
+ *   l_i   = sum_{visible j} exp(S_ij - m_i)
+ *   O_i   = sum_{visible j} exp(S_ij - m_i) v_j / l_i
+ *   LSE_i = m_i + ln(l_i)
+ *
+ * Sources: Saraf, "FlashAttention 2: Three Places the Chip Was Still
+ * Waiting" -- section 1 (tiles folded into a running result with a running
+ * max and denominator, exact), section 2.2 (the max correction every step,
+ * the division once per query block), section 2.3 (query blocks as
+ * independent units of parallel work), section 2.4 (each wave owns whole
+ * query rows); papermap "FlashAttention-2" explainer, Chapter 02 (same
+ * outputs as standard attention, the N x N matrix never materialised);
+ * Mishra, "FlashAttention-2 and -3: From Algebra to GPU Scheduling", "How
+ * to compare kernels honestly" (dtype, head dim, lengths, batch, heads and
+ * causal mode are the parameters of a forward call).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major, contiguous: q, k, v, o are [B, H, N, d]
+ *     (d fastest), lse is [B, H, N].  Query and key lengths are both N.
+ *   - All data pointers are DEVICE pointers on the current HIP device.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; it enqueues its kernels on `stream` and returns.  The
+ *     caller observes completion through the stream.
+ *   - o and lse are fully overwritten (every row, including ragged tails);
+ *     q, k and v are only read.  Outputs must not alias inputs.
+ *   - Arguments are validated before any HIP call; on error nothing is
+ *     launched and a negative fa2_status is returned.  No output is printed
+ *     and no exception crosses the ABI.
+ *   - The library keeps no mutable global state and is re-entrant.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA2_VERSION 100 /* major*100 + minor */
+
+typedef enum fa2_dtype {
+  FA2_F32 = 0,  /* IEEE binary32 */
+  FA2_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+} fa2_dtype;
+
+typedef enum fa2_status {
+  FA2_OK = 0,
+  FA2_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad size, bad scale, bad dtype code */
+  FA2_ERR_UNSUPPORTED = -2, /* valid arguments outside what the kernels implement (head dim, dtype pair) */
+  FA2_ERR_NO_DEVICE = -3,   /* no usable HIP device is current */
+  FA2_ERR_LAUNCH = -4       /* the kernel launch was rejected by the runtime */
+} fa2_status;
+
+/*
+ * fa2_fwd -- attention forward: O and the per-row logsumexp.
+ *
+ *   q, k, v   device pointers, [B, H, N, d] in `in_dtype`, 16-byte aligned.
+ *   o         device pointer, [B, H, N, d] in `o_dtype`, 16-byte aligned.
+ *   lse       device pointer, [B, H, N] float32, 4-byte aligned: natural-log
+ *             logsumexp of the scaled visible scores of each query row.
+ *   B, H, N   batch, heads, sequence length; each >= 1, and B*H*N*d must
+ *             fit in a signed 64-bit integer (offsets are 64-bit).
+ *   d         head dimension; 64 or 128 (others: FA2_ERR_UNSUPPORTED).
+ *   causal    0: every key visible; 1: key j visible to query i iff j <= i.
+ *   scale     finite, >= 0; multiplies the raw dot products (typically
+ *             1/sqrt(d)).  Negative or non-finite: FA2_ERR_INVALID_ARG.
+ *   stream    a hipStream_t cast to void* (NULL = the null stream).
+ *   in_dtype  FA2_BF16 or FA2_F32 for q, k and v.
+ *   o_dtype   FA2_F32 or FA2_BF16 for o.  bf16 outputs are rounded to
+ *             nearest-even from the fp32 result.
+ *
+ * Arithmetic: bf16 inputs use bf16 matrix-core products with fp32
+ * accumulation, the softmax statistics in fp32, and probabilities rounded
+ * to bf16 (nearest-even) before the P*V product.  fp32 inputs keep every
+ * step in fp32.
+ *
+ * Returns FA2_OK after enqueueing, else a negative fa2_status.
+ */
+int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            int B, int H, int N, int d, int causal, float scale,
+            void* stream, int in_dtype, int o_dtype);
+
+/*
+ * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,
+ * for reporting and tests.  Host-only; touches no device.
+ */
+typedef struct fa2_plan_t {
+  int block_rows;          /* B_r: query rows per workgroup */
+  int block_cols;          /* B_c: keys per K/V tile */
+  int waves_per_group;     /* wavefronts per workgroup (each owns B_r/waves rows) */
+  int query_tiles;         /* ceil(N / B_r): query tiles per (batch, head) */
+  long long workgroups;    /* B*H*query_tiles: the grid size */
+  long long tile_pairs;    /* (query tile, key tile) pairs the grid executes */
+  long long normalisations;/* accumulator divisions: one per query tile */
+  double waves_of_groups;  /* workgroups / num_units (0 if num_units == 0) */
+  int last_wave_groups;    /* workgroups in the final, partial wave (0 if none/unknown) */
+  double flops_executed;   /* matrix-core flops the executed tile pairs cost */
+  double flops_credited;   /* 4*B*H*N*N*d, halved when causal */
+} fa2_plan_t;
+
+/*
+ * fa2_plan -- fill *out with the geometry for a forward call.
+ *
+ *   block_rows  0 = the library's own tile height for (d, in_dtype);
+ *               > 0 = evaluate that tile height instead (analysis only:
+ *               fa2_fwd always uses the library's own tiles).
+ *   block_cols  0 = the library's own key-tile width; > 0 overrides it.
+ *   num_units   number of compute units to express the grid in waves of
+ *               workgroups (one resident workgroup per unit); 0 = skip.
+ *
+ * Saraf, section 2.3: one block per (sequence, head) versus one block per
+ * query tile per (sequence, head); section 2.2: one division per query
+ * block.  Returns FA2_OK or FA2_ERR_INVALID_ARG / FA2_ERR_UNSUPPORTED under
+ * the same size rules as fa2_fwd.
+ */
+int fa2_plan(int B, int H, int N, int d, int causal, int in_dtype,
+             int block_rows, int block_cols, int num_units, fa2_plan_t* out);
+
+/* fa2_strerror -- static, NUL-terminated description of a status code. */
+const char* fa2_strerror(int status);
+
+/* fa2_version -- FA2_VERSION of the built library. */
+int fa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (per workload dtype): bf16 inputs -> max |O - O_ref| <= 1e-2 and
+max |LSE - LSE_ref| <= 1e-3 with fp32 O; fp32 inputs -> both <= 1e-5.
+bf16 O is additionally allowed half a bf16 ulp of the reference value for
+its own rounding.
+
+* small shapes spanning several tiles and ragged tails: every element;
+* the five workloads at full size, in the launch configuration the
+  benchmark times: sampled rows (first/last rows, tile edges, random rows of
+  several heads), each row computed by the oracle one by one;
+* closed forms and invariants run on the GPU;
+* bitwise run-to-run determinism and a non-default stream.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_33_amd as fa2
+import oracle.exact_attention as ref
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (1e-2, 1e-3), "fp32": (1e-5, 1e-5)}
+DEV = "cuda:0"
+
+
+def _np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _run(q, k, v, causal, scale, o_dtype=torch.float32):
+    o, lse = fa2.forward(q, k, v, causal=causal, scale=scale, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _bf16_half_ulp(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)  # half of 2^(e-7)
+
+
+def _check(o, lse, eo, el, dtype, what, o_bf16=False):
+    to, tl = TOL[dtype]
+    o = _np64(o)
+    lse = _np64(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"{what}: non-finite output"
+    err_o = np.abs(o - eo)
+    bound = to + (_bf16_half_ulp(eo) if o_bf16 else 0.0)
+    eo_max = float(np.max(err_o)) if err_o.size else 0.0
+    el_max = float(np.max(np.abs(lse - el))) if lse.size else 0.0
+    print(f"[parity] {what}: max|dO|={eo_max:.3e} max|dLSE|={el_max:.3e}", flush=True)
+    assert np.all(err_o <= bound), f"{what}: O err {eo_max:.3e} > {to}"
+    assert el_max <= tl, f"{what}: LSE err {el_max:.3e} > {tl}"
+
+
+def _inputs(B, H, N, d, dtype, seed, outliers=0.0):
+    w = workloads.Workload("adhoc", B, H, N, d, dtype, 1.0 / math.sqrt(d), False,
+                           outliers, 20.0 if outliers else 1.0)
+    return workloads.make_inputs(w, seed, device=DEV)
+
+
+# --- small shapes, every element ---------------------------------------------
+
+SMALL = [
+    # B, H, N, d, dtype, causal
+    (1, 1, 1, 64, "bf16", False), (1, 1, 1, 128, "bf16", True),
+    (1, 2, 3, 64, "bf16", True), (2, 1, 3, 128, "bf16", False),
+    (1, 2, 127, 64, "bf16", True), (1, 2, 127, 128, "bf16", False),
+    (2, 1, 129, 64, "bf16", False), (1, 2, 129, 128, "bf16", True),
+    (1, 2, 1000, 64, "bf16", True), (1, 2, 1000, 128, "bf16", False),
+    (2, 3, 777, 128, "bf16", True), (1, 1, 2048, 128, "bf16", True),
+    (1, 1, 1, 64, "fp32", False), (1, 1, 3, 128, "fp32", True),
+    (1, 2, 127, 64, "fp32", True), (1, 1, 129, 128, "fp32", False),
+    (1, 2, 1000, 64, "fp32", False), (1, 1, 1000, 128, "fp32", True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", SMALL,
+                         ids=[f"{b}x{h}x{n}x{d}-{dt}-{'causal' if c else 'full'}" for b, h, n, d, dt, c in SMALL])
+def test_small_shapes_every_element(B, H, N, d, dtype, causal):
+    q, k, v = _inputs(B, H, N, d, dtype, seed=N + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _run(q, k, v, causal, scale)
+    eo, el = ref.attention_ref(_np64(q), _np64(k), _np64(v), scale, causal)
+    _check(o, lse, eo, el, dtype, f"{B}x{H}x{N}x{d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_output(dtype, causal):
+    q, k, v = _inputs(1, 2, 300, 128, dtype, seed=3)
+    o, lse = _run(q, k, v, causal, 0.088, o_dtype=torch.bfloat16)
+    assert o.dtype == torch.bfloat16
+    eo, el = ref.attention_ref(_np64(q), _np64(k), _np64(v), 0.088, causal)
+    _check(o, lse, eo, el, "bf16", f"bf16 O from {dtype} causal={causal}", o_bf16=True)
+
+
+def test_outliers_small():
+    # the long-causal recipe (0.1% of Q/K entries x20) at a size the oracle does whole
+    q, k, v = _inputs(1, 4, 1024, 128, "bf16", seed=0, outliers=0.001)
+    o, lse = _run(q, k, v, True, 1.0 / math.sqrt(128))
+    eo, el = ref.attention_ref(_np64(q), _np64(k), _np64(v), 1.0 / math.sqrt(128), True)
+    _check(o, lse, eo, el, "bf16", "outliers 1x4x1024x128 causal")
+
+
+# --- the five workloads at full size, sampled rows ----------------------------
+
+def _sample_rows(N, rng, n_random=40):
+    edges = [0, 1, 2, N - 1, N - 2]
+    for t in (63, 64, 127, 128, 129, 255, 256):
+        if t < N:
+            edges.append(t)
+    rows = set(int(r) for r in edges if 0 <= r < N)
+    rows.update(int(r) for r in rng.integers(0, N, size=min(n_random, N)))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_full_size(name, seed):
+    w = workloads.get(name)
+    print(f"[parity] workload {name} seed {seed} shape {w.shape} {w.dtype} causal={w.causal}", flush=True)
+    q, k, v = workloads.make_inputs(w, seed, device=DEV)
+    o, lse = _run(q, k, v, w.causal, w.scale)
+    rng = np.random.default_rng(seed + 100)
+    if w.B * w.H * w.N <= 128 * 64:
+        eo, el = ref.attention_ref(_np64(q), _np64(k), _np64(v), w.scale, w.causal)
+        _check(o, lse, eo, el, w.dtype, f"{name} seed {seed} (all rows)")
+        return
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(heads) < min(4, w.B * w.H):
+        heads.add((int(rng.integers(0, w.B)), int(rng.integers(0, w.H))))
+    for b, h in sorted(heads):
+        rows = _sample_rows(w.N, rng)
+        eo, el = ref.attention_rows(_np64(q[b, h]), _np64(k[b, h]), _np64(v[b, h]), w.scale, w.causal, rows)
+        _check(o[b, h][rows], lse[b, h][rows], eo, el, w.dtype, f"{name} seed {seed} head ({b},{h}) {len(rows)} rows")
+    # properties that hold at any size: finite everywhere, LSE >= max visible score (cheap bound)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+# --- closed forms and invariants on the GPU -----------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_closed_form(dtype, causal):
+    q, k, v = _inputs(1, 2, 333, 64, dtype, seed=4)
+    o, lse = _run(q, k, v, causal, 0.0)
+    vv = _np64(v)
+    n = np.arange(1, 334)
+    eo = np.cumsum(vv, axis=2) / n[None, None, :, None] if causal else np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+    el = np.broadcast_to(np.log(n) if causal else np.full(333, math.log(333)), (1, 2, 333))
+    _check(o, lse, eo, el, dtype, f"scale=0 {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_constant_v(d):
+    q, k, _ = _inputs(1, 2, 500, d, "bf16", seed=5)
+    c = torch.linspace(-2, 2, d).to(torch.bfloat16)
+    v = c.to(DEV).expand(1, 2, 500, d).contiguous()
+    for causal in (False, True):
+        o, _ = _run(q, k, v, causal, 1.0 / math.sqrt(d))
+        err = (o.cpu().double() - c.double()).abs().max().item()
+        print(f"[parity] constant V d={d} causal={causal}: {err:.3e}", flush=True)
+        assert err <= 1e-2
+
+
+def test_kv_permutation_noncausal():
+    q, k, v = _inputs(1, 2, 640, 128, "bf16", seed=6)
+    perm = torch.randperm(640, generator=torch.Generator().manual_seed(0)).to(DEV)
+    o1, l1 = _run(q, k, v, False, 0.09)
+    o2, l2 = _run(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), False, 0.09)
+    assert (o1 - o2).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+def test_key_shift_exact_inputs():
+    # entries in {-1,-.5,0,.5,1} and an integer shift keep every value exact in bf16
+    g = torch.Generator().manual_seed(8)
+    vals = torch.tensor([-1.0, -0.5, 0.0, 0.5, 1.0])
+    pick = lambda: vals[torch.randint(0, 5, (1, 1, 256, 64), generator=g)]  # noqa: E731
+    q, k, v = (pick().to(torch.bfloat16).to(DEV) for _ in range(3))
+    u = torch.randint(-1, 2, (64,), generator=g).float()
+    k2 = (k.float().cpu() + u).to(torch.bfloat16).to(DEV)
+    assert torch.equal(k2.float().cpu(), k.float().cpu() + u)
+    for causal in (False, True):
+        o1, l1 = _run(q, k, v, causal, 0.125)
+        o2, l2 = _run(q, k2, v, causal, 0.125)
+        shift = 0.125 * (q.float().cpu()[0, 0] @ u)
+        assert (o1 - o2).abs().max().item() <= 1e-2
+        assert (l2.cpu()[0, 0] - l1.cpu()[0, 0] - shift).abs().max().item() <= 1e-3
+
+
+def test_causal_prefix_and_first_row():
+    q, k, v = _inputs(1, 2, 1024, 128, "bf16", seed=9)
+    o, l = _run(q, k, v, True, 0.088)
+    for m in (1, 128, 300):
+        op, lp = _run(q[:, :, :m].contiguous(), k[:, :, :m].contiguous(), v[:, :, :m].contiguous(), True, 0.088)
+        assert (o[:, :, :m] - op).abs().max().item() <= 1e-2
+        assert (l[:, :, :m] - lp).abs().max().item() <= 1e-3
+    # row 0 sees only key 0
+    assert (o[:, :, 0].float() - v[:, :, 0].float()).abs().max().item() <= 1e-6
+    l0 = 0.088 * (q[:, :, 0].float() * k[:, :, 0].float()).sum(-1)
+    assert (l[:, :, 0] - l0).abs().max().item() <= 1e-4
+
+
+def test_deterministic_and_stream():
+    q, k, v = _inputs(2, 2, 1111, 128, "bf16", seed=10)
+    o1, l1 = _run(q, k, v, True, 0.088)
+    o2, l2 = _run(q, k, v, True, 0.088)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o3, l3 = fa2.forward(q, k, v, causal=True, scale=0.088)
+    s.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_outputs_fully_overwritten():
+    q, k, v = _inputs(1, 1, 200, 64, "bf16", seed=11)
+    o = torch.full((1, 1, 200, 64), float("nan"), device=DEV)
+    lse = torch.full((1, 1, 200), float("nan"), device=DEV)
+    fa2.forward(q, k, v, causal=True, scale=0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+
+
+def test_error_status_on_gpu():
+    q = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa2.Fa2Error) as e:
+        fa2.forward(q, q.clone(), q.clone())
+    assert e.value.status == fa2.FA2_ERR_UNSUPPORTED
