@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention-2 forward (HIP path) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fa2_fwd call over one batch of the workload (default: the
+headline workload, long_causal = bf16 [B=2, H=16, N=8192, d=128], causal,
+0.1% of Q/K entries x20, fp32 O).  Inputs are seeded, synthetic and already
+resident in device memory when timing starts.  W untimed steps, then K
+timed steps bracketed by device synchronisation; each launch is also
+bracketed by HIP events recorded on the stream the kernel runs on.
+
+Prints ONE JSON line: throughput in TFLOP/s of credited work
+(4*B*H*N^2*d, halved when causal), the roofline of the attention kernel
+against the MI355X dense-bf16 matrix peak, the HBM traffic measured by
+rocprofv3 counters (from the committed summary, if it matches the current
+kernel source), and the fp64 CPU oracle timed on a bounded sample of the
+same workload on the host cores.
+
+Extra modes used to produce committed profile summaries:
+    --calibrate-copy      time a plain 1 GiB device copy (counter calibration)
+    --summarize-pmc DIR   summarise rocprofv3 --pmc CSV output found under DIR
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPs/s and % of MI355X bf16 MFMA peak, d=128 N=8k causal"
+# Dense bf16 matrix-core peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_fwd_bf16.hip",
+                  "exact_tiled_attention_33_amd/csrc/fa2_fwd_f32.hip",
+                  "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
+                  "exact_tiled_attention_33_amd/csrc/fa2_launch.h"]
+CALIB_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_hbm.md, if it
+    was measured on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa2_fwd_{workload}_hbm.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole heads of the workload until the budget
+    is used (at least one head).  Returns the cpu_baseline object."""
+    import numpy as np
+    import torch
+
+    import oracle.exact_attention as ref
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_total = 0, 0.0
+    for b, h in heads:
+        qh = q[b, h].to("cpu", torch.float64).numpy()
+        kh = k[b, h].to("cpu", torch.float64).numpy()
+        vh = v[b, h].to("cpu", torch.float64).numpy()
+        t0 = time.perf_counter()
+        ref.attention_head(qh, kh, vh, w.scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    import workloads
+
+    flops = workloads.credited_flops(1, done, w.N, w.d, w.causal)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} (batch, head) pairs of {w.name}, whole heads "
+                  f"(N={w.N}, d={w.d}, causal={w.causal}), fp64 numpy, {t_total:.1f} s",
+        "seconds": t_total,
+    }
+
+
+def run_bench(args) -> dict:
+    import torch
+
+    import exact_tiled_attention_33_amd as fa2
+    import workloads
+
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    q, k, v = workloads.make_inputs(w, seed=args.seed, device=dev)
+    o_dtype = torch.bfloat16 if args.o_dtype == "bf16" else torch.float32
+    o = torch.empty(w.shape, dtype=o_dtype, device=dev)
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    in_code = fa2.BF16 if w.dtype == "bf16" else fa2.F32
+    o_code = fa2.BF16 if args.o_dtype == "bf16" else fa2.F32
+    handle = stream.cuda_stream
+    call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 w.B, w.H, w.N, w.d, int(w.causal), w.scale, handle, in_code, o_code)
+    torch.cuda.synchronize()
+
+    def step():
+        st = fa2.fa2_fwd(*call_args)
+        if st != fa2.FA2_OK:
+            raise fa2.Fa2Error(st)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    span_ms = starts[0].elapsed_time(ends[-1])
+
+    flops = workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = traffic_from_profiles(w.name)
+    plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+            "scale": w.scale, "in_dtype": w.dtype, "o_dtype": args.o_dtype,
+            "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
+            "dropout": 0.0, "backward": False, "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(peak, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_ms_avg": round(avg_launch_ms, 4),
+            "algorithmic_flops_per_launch": flops,
+            "executed_flops_per_launch": plan["flops_executed"],
+        },
+        "timing": {"events_span_ms": round(span_ms, 4), "wall_s": round(wall, 4),
+                   "per_launch_ms_min": round(min(per_launch_ms), 4),
+                   "per_launch_ms_max": round(max(per_launch_ms), 4)},
+        "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                "cus": props.multi_processor_count},
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "context_not_target": "pages (A100): FA1 25-40% of peak, FA2 50-73% of peak, up to 230 TFLOP/s",
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, budget_s=args.cpu_budget)
+    return result
+
+
+def calibrate_copy(args) -> None:
+    """A plain device-to-device copy of CALIB_BYTES, repeated: its counter
+    readings calibrate FETCH_SIZE / WRITE_SIZE against known bytes."""
+    import torch
+
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": CALIB_BYTES, "repeats": args.steps}))
+
+
+def summarize_pmc(root: str) -> None:
+    """Average per-dispatch counter values (KiB) per kernel from rocprofv3
+    --pmc CSV output under ``root``."""
+    import csv
+
+    rows = []
+    for path in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "?")
+        ctr = r.get("Counter_Name", "?")
+        val = float(r.get("Counter_Value", "nan"))
+        key = (name[:90], ctr)
+        acc.setdefault(key, []).append(val)
+    for (name, ctr), vals in sorted(acc.items()):
+        print(f"{ctr}\t{len(vals)} dispatches\tmean {sum(vals) / len(vals):.1f} KiB\t{name}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--o-dtype", choices=["fp32", "bf16"], default="fp32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-pmc", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the attention forward on exactly one GPU; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported. "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return 0
+    import workloads
+
+    if args.workload is None:
+        args.workload = workloads.HEADLINE
+    result = run_bench(args)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
