@@ -69,6 +69,10 @@ def build(verbose: bool = False) -> Path:
     out = _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", str(tmp)])
     if verbose and out.strip():
         print(out)
+    # resolve every symbol now, so a kernel whose host stub was not emitted
+    # fails the build instead of the first load
+    import ctypes
+    ctypes.CDLL(str(tmp), mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, LIB)
     return LIB
 

@@ -22,8 +22,8 @@ struct FwdArgs {
 // Tile geometry of each kernel family.  The bf16 kernel gives every
 // wavefront 32 query rows (the N side of a 32x32 MFMA) and streams keys in
 // tiles of kBf16BlockCols; the fp32 kernel does the same with 32-key tiles.
-constexpr int kBf16Waves = 4;
-constexpr int kBf16BlockRows = kBf16Waves * 32;  // 128
+constexpr int kBf16Waves = 8;
+constexpr int kBf16BlockRows = kBf16Waves * 32;  // 256
 constexpr int kBf16BlockCols = 64;
 constexpr int kF32Waves = 4;
 constexpr int kF32BlockRows = kF32Waves * 32;    // 128

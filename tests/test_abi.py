@@ -151,8 +151,9 @@ def test_pages_score_matrix_size():
 def test_own_plan_for_the_workloads():
     import workloads
     mi355x_cus = 256
-    expect_groups = {"fp32_small": 1, "short_seq": 2048, "mid_seq": 2048, "long_causal": 2048,
-                     "long_few_head": 512}
+    # bf16: 256-row query tiles; fp32: 128-row query tiles
+    expect_groups = {"fp32_small": 1, "short_seq": 1024, "mid_seq": 1024, "long_causal": 1024,
+                     "long_few_head": 256}
     for name, w in workloads.WORKLOADS.items():
         code = fa2.BF16 if w.dtype == "bf16" else fa2.F32
         p = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), code, num_units=mi355x_cus)
@@ -160,8 +161,8 @@ def test_own_plan_for_the_workloads():
         assert p["flops_credited"] == workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal)
         assert p["flops_executed"] >= p["flops_credited"]
         if w.causal:
-            # above-diagonal key tiles are skipped: executed work stays within 2% of credited
-            assert p["flops_executed"] / p["flops_credited"] < 1.02, name
+            # above-diagonal key tiles are skipped: executed work stays within 4% of credited
+            assert p["flops_executed"] / p["flops_credited"] < 1.04, name
         else:
             assert p["flops_executed"] == p["flops_credited"]
 
