@@ -42,13 +42,14 @@
 // j, then O += V P of tile j-1: 32 MFMAs) while the other is in a vector
 // phase (mask, row max, correction, exp2, row sum, bf16 packing of tile j),
 // so each SIMD always has MFMA and VALU work from different wavefronts.
-// K/V tiles are fetched into registers four phases before use, written to
-// 2-deep LDS rings two phases later, and read by both groups.
+// K/V tiles are copied from global memory straight into 3-deep (padded) LDS
+// rings four phases before they are first read, and read by both groups.
 
 #include "fa2_launch.h"
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 namespace fa2 {
 namespace {
@@ -58,6 +59,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -67,30 +69,33 @@ constexpr int kRows = 32;               // query rows per wavefront
 constexpr int kBr = kBf16BlockRows;     // query rows per workgroup
 constexpr int kBc = kBf16BlockCols;     // keys per K/V tile
 constexpr int kThreads = kWaves * 64;
-constexpr int kRing = 2;                // K and V tiles resident per ring
+constexpr int kRing = 3;                // K and V tiles resident per ring
 
 template <int D>
 struct Geo {
-  // K and V tiles are stored unpadded (64 rows x 2*D bytes) with the 16-byte
-  // chunks of each row permuted by an XOR swizzle, so that both the tile
-  // writes (1 KiB contiguous per wave instruction) and the operand reads are
-  // free of bank conflicts:
-  //  * K operand reads (b128): 16 lanes of a phase read 16 consecutive rows
-  //    at the same logical chunk -> swizzle by row spreads them over 16
-  //    distinct 16-byte slots of a 256-byte bank line;
-  //  * V transposing reads: a half-wave reads 4 rows x 64 bytes -> swizzle
-  //    by (row % 4) moves each row's 4 chunks to a distinct quarter line.
+  // LDS rows are padded so that every operand read is free of bank conflicts
+  // and every per-lane address is one base register plus an immediate:
+  //  * K (stride 2*D + 16 bytes): the 16 lanes of a b128 read phase read 16
+  //    consecutive rows at the same column, which the 16-byte pad spreads
+  //    over 16 distinct 16-byte slots of a 256-byte bank line;
+  //  * V (stride 2*D + 64 bytes): a half-wave transposing read touches 4
+  //    rows x 64 bytes, which the 64-byte pad puts on 4 disjoint quarters.
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kTileBytes = kBc * kRowBytes;
-  static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
-  static constexpr int kRowsPerInst = 1024 / kRowBytes;     // rows per 1 KiB wave write
-  static constexpr int kRowsPerWave = kBc / kWaves;         // tile rows each wave loads
-  static constexpr int kInstPerWave = kRowsPerWave / kRowsPerInst;
+  static constexpr int kStrideK = kRowBytes + 16;
+  static constexpr int kStrideV = kRowBytes + 64;
+  static constexpr int kTileK = kBc * kStrideK;
+  static constexpr int kTileV = kBc * kStrideV;
+  static constexpr int kLdsBytes = kRing * (kTileK + kTileV);
+  static constexpr int kChunks = kRowBytes / 16;            // 16-byte data chunks per row
+  // A tile is copied by 64-lane instructions that each fill 64 consecutive
+  // 16-byte LDS slots (pad slots included); instruction i goes to wave i % 8.
+  static constexpr int kSlotsK = kStrideK / 16;              // 16-byte slots per K row
+  static constexpr int kSlotsV = kStrideV / 16;
+  static constexpr int kInstK = kBc * kSlotsK / 64;
+  static constexpr int kInstV = kBc * kSlotsV / 64;
+  static_assert(kBc * kSlotsK % 64 == 0 && kBc * kSlotsV % 64 == 0, "tiles must fill whole instructions");
   static constexpr int kKSteps = D / 16;                    // k-steps of the score MFMA
   static constexpr int kDBlocks = D / 32;                   // 32-row blocks of O^T
-  static_assert(kRowsPerWave % kRowsPerInst == 0, "tile rows must split evenly");
-  __device__ static constexpr int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-  __device__ static constexpr int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ float max_halves(float x) {
@@ -106,13 +111,78 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 // Raw buffer resource over [base, base + bytes): loads past the end return
 // zeros, which is how ragged key tiles and query tails are handled without
-// branches.
+// branches.  Both arguments must be wave-uniform; the size is passed through
+// readfirstlane because clamps like max(0, min(a, b)) are selected as VALU
+// instructions, and a descriptor in vector registers would turn every load
+// into a loop over lanes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kAhead = 4;  // LDS operand reads in flight ahead of the MFMAs
+
+// Schedule n_mfma MFMAs, each needing `reads` LDS reads, so that the reads
+// run kAhead MFMAs ahead of their consumer.
+template <int kNMfma, int kReads>
+__device__ __forceinline__ void sched_reads_ahead() {
+#pragma unroll
+  for (int n = 0; n < kAhead; ++n) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+#pragma unroll
+  for (int n = 0; n < kNMfma; ++n) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (n + kAhead < kNMfma) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+  }
+}
+
+// Raw buffer descriptor as four scalar registers, for the LDS copy below.
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  i32x4 r = {__builtin_amdgcn_readfirstlane((int)(b & 0xffffffffu)),
+             __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu)),
+             __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+  return r;
+}
+
+// Copy 16 bytes per lane from global memory (buffer rsrc, byte offset
+// voff; zeros past the end) straight into LDS: lane i's bytes land at LDS
+// byte offset lds_offset + 16*i (lds_offset is wave-uniform).  Written as inline assembly so that the compiler does not
+// treat every later LDS read as dependent on the copy (it would wait for all
+// outstanding copies); completion is tracked explicitly with wait_vmem and
+// published with a workgroup barrier.  Clobbers m0, which nothing else in
+// these kernels uses.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, int voff, unsigned lds_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_offset), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Byte offset of a __shared__ address within the workgroup's LDS.
+__device__ __forceinline__ unsigned lds_offset_of(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// s_waitcnt (gfx9 encoding): wait until at most n vector-memory operations
+// of this wave are outstanding; LDS and export counters are left alone.
+__device__ __forceinline__ void wait_vmem(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+  }
 }
 
 // Max-correction threshold, in log2 units: the reference max of a row is
@@ -128,9 +198,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int T, float c) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kRing * G::kTileBytes];
+  // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
+  __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
   char* const lds_k = smem;
-  char* const lds_v = smem + kRing * G::kTileBytes;
+  char* const lds_v = smem + kRing * G::kTileK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,43 +251,55 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     n_full = min(n_full, (qw + 1) / kBc);
   }
 
-  // Tile staging: each wave fetches kInstPerWave x 1 KiB of a K tile and of a
-  // V tile into registers, and later writes them to LDS.  Lane -> (row,
-  // stored slot); it fetches the logical chunk that the swizzle puts in that
-  // slot, so the LDS writes are contiguous.  Keys past N read as zeros.
-  const int ld_row = wave * G::kRowsPerWave + lane / G::kChunks;
-  const int ld_slot = lane % G::kChunks;
-  u32x4 stage_k[G::kInstPerWave], stage_v[G::kInstPerWave];
-  auto fetch_tile = [&](const __bf16* src, u32x4 (&dst)[G::kInstPerWave], int j, bool is_k) {
-    const int key0 = j * kBc;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (long long)key0 * D, min(kBc, N - key0) * G::kRowBytes);
+  // Tile copies: instruction i of a tile fills LDS slots [64i, 64i + 64);
+  // slot u is (row u / slots-per-row, chunk u % slots-per-row), and the
+  // lanes that land on a row's pad slots fetch that row's chunk 0 (any
+  // in-range address would do).  Keys past N read as zeros.  Instruction i
+  // is issued by wave i % 8; the per-lane source offsets do not depend on
+  // the tile and are computed once.
+  constexpr int kCopyK = (G::kInstK + kWaves - 1) / kWaves;
+  constexpr int kCopyV = (G::kInstV + kWaves - 1) / kWaves;
+  int voff_k[kCopyK], voff_v[kCopyV];
 #pragma unroll
-    for (int i = 0; i < G::kInstPerWave; ++i) {
-      const int row = ld_row + i * G::kRowsPerInst;
-      const int chunk = ld_slot ^ (is_k ? G::swz_k(row) : G::swz_v(row));
-      dst[i] = load16(r, row * G::kRowBytes + chunk * 16);
+  for (int k = 0; k < kCopyK; ++k) {
+    const int u = (wave + k * kWaves) * 64 + lane;
+    const int chunk = u % G::kSlotsK;
+    voff_k[k] = (u / G::kSlotsK) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
+  }
+#pragma unroll
+  for (int k = 0; k < kCopyV; ++k) {
+    const int u = (wave + k * kWaves) * 64 + lane;
+    const int chunk = u % G::kSlotsV;
+    voff_v[k] = (u / G::kSlotsV) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
+  }
+  const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
+  const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
+  auto copy_tile = [&](const __bf16* src, int slot, int j, auto is_k) __attribute__((always_inline)) {
+    constexpr bool K_TILE = decltype(is_k)::value;
+    constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
+    constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
+    const int key0 = j * kBc;
+    const i32x4 r = raw_rsrc(src + (long long)key0 * D, min(kBc, N - key0) * G::kRowBytes);
+    const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
+#pragma unroll
+    for (int k = 0; k < kCopy; ++k) {
+      if (wave + k * kWaves < kInst)
+        copy16_to_lds(r, K_TILE ? voff_k[k] : voff_v[k], base + k * kWaves * 1024);
     }
   };
-  auto store_tile = [&](const u32x4 (&src)[G::kInstPerWave], char* dst) {
-#pragma unroll
-    for (int i = 0; i < G::kInstPerWave; ++i)
-      *(u32x4*)(dst + (ld_row + i * G::kRowsPerInst) * G::kRowBytes + ld_slot * 16) = src[i];
-  };
+  // copy instructions this wave issues per K (V) tile
+  const int n_copy_k = (G::kInstK - wave + kWaves - 1) / kWaves;
+  const int n_copy_v = (G::kInstV - wave + kWaves - 1) / kWaves;
 
-  // Per-lane LDS offsets.  K operand (kb, s): row 32*kb + l32, logical
-  // chunk 2*s + half.  V transposing read for (db, kb, h, u): lane i of each
-  // 16-lane group points at key row (i / 4) of a 4-row slab and dcol
-  // 4*(i % 4) of a 16-column slab; lane i then receives the 4 keys of one
-  // dcol (lane % 32).
-  auto k_off = [&](int kb, int s) {
-    const int r = 32 * kb + l32;
-    return r * G::kRowBytes + (((2 * s + half) ^ G::swz_k(r)) * 16);
-  };
-  auto v_off = [&](int db, int kb, int h, int u) {
-    const int r = 32 * kb + 16 * h + 8 * u + 4 * half + ((lane & 15) >> 2);
-    const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    return r * G::kRowBytes + ((chunk ^ G::swz_v(r)) * 16) + 8 * (lane & 1);
-  };
+  // Per-lane LDS offsets; everything else is an immediate.  K operand
+  // (kb, s): row 32*kb + l32, columns 16*s + 8*half .. +7.  V transposing
+  // read for (db, kb, h, u): lane i of each 16-lane group points at key row
+  // (i / 4) of a 4-row slab and dcol 4*(i % 4) of a 16-column slab; lane i
+  // then receives the 4 keys of one dcol (lane % 32).
+  const int k_lane = l32 * G::kStrideK + 16 * half;
+  const int v_lane = (4 * half + ((lane & 15) >> 2)) * G::kStrideV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  auto k_off = [&](int kb, int s) __attribute__((always_inline)) { return k_lane + 32 * kb * G::kStrideK + 32 * s; };
+  auto v_off = [&](int db, int kb, int h, int u) __attribute__((always_inline)) { return v_lane + (32 * kb + 16 * h + 8 * u) * G::kStrideV + 64 * db; };
 
   f32x16 oacc[G::kDBlocks];
 #pragma unroll
@@ -232,12 +315,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // No branches here: for tiles past a wavefront's last row the scores are
   // computed but fully masked in the vector phase, so their P is 0.
   // Operands are read from LDS kAhead MFMAs ahead of their use.
-  constexpr int kAhead = 4;
-  auto scores_mfma = [&](int j) {
-    const char* kbuf = lds_k + (j % kRing) * G::kTileBytes;
+  auto scores_mfma = [&](const char* kbuf) __attribute__((always_inline)) {
     // MFMA n uses k-step s = n / 2 of block kb = n % 2 (two independent chains).
     constexpr int kN = 2 * G::kKSteps;
-    auto read_k = [&](int n) { return *(const bf16x8*)(kbuf + k_off(n & 1, n >> 1)); };
+    auto read_k = [&](int n) __attribute__((always_inline)) { return *(const bf16x8*)(kbuf + k_off(n & 1, n >> 1)); };
     bf16x8 ka[kAhead];
 #pragma unroll
     for (int n = 0; n < kAhead; ++n) ka[n] = read_k(n);
@@ -248,12 +329,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       sacc[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n >> 1], n < 2 ? f32x16{} : sacc[n & 1], 0, 0, 0);
     }
   };
-  auto pv_mfma = [&](int j) {
+  auto pv_mfma = [&](const char* vbuf) __attribute__((always_inline)) {
     // Key step (kb, h) covers keys 32*kb + 16*h + {0..15}; operand slot u
     // of lane (l32, half) is key 8*(u/4) + 4*half + (u%4) in both the P^T
     // operand (accumulator elements 8h..8h+7) and the V^T one.  MFMA n uses
     // key step n / kDBlocks on O^T block n % kDBlocks.
-    const char* vbuf = lds_v + (j % kRing) * G::kTileBytes;
     constexpr int kN = 4 * G::kDBlocks;
     auto read_v = [&](int n, bf16x4 (&dst)[2]) {
       const int db = n % G::kDBlocks, kb = (n / G::kDBlocks) >> 1, h = (n / G::kDBlocks) & 1;
@@ -271,15 +351,23 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
     }
   };
-  auto matrix_phase = [&](int j) {
+  // Tile j's K is in ring slot j % 3, tile j-1's V in slot (j - 1) % 3; the
+  // slot is a compile-time constant in each third of the unrolled loops
+  // below, so every LDS address is a base register plus an immediate.
+  auto matrix_phase = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
     __builtin_amdgcn_s_setprio(1);
-    scores_mfma(j);
-    pv_mfma(j - 1);  // P of tile -1 is all zeros
+    scores_mfma(lds_k + S * G::kTileK);
+    pv_mfma(lds_v + ((S + kRing - 1) % kRing) * G::kTileV);
+    // Keep each operand read kAhead MFMAs ahead of its use: LDS latency
+    // (~70 cycles unloaded) exceeds one MFMA (32 cycles).
+    sched_reads_ahead<2 * G::kKSteps, 1>();
+    sched_reads_ahead<4 * G::kDBlocks, 2>();
     __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- vector phase of tile j: mask, row max, correction, P = exp2(...) ----
-  auto vector_phase = [&](int j) {
+  auto vector_phase = [&](int j) __attribute__((always_inline)) {
     if (j >= n_full) {
       // element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*half + (i%4);
       // tiles at or past n_w lie wholly above this wave's rows -> all masked
@@ -327,69 +415,104 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     l += rs;
   };
 
-  // ---- prologue: K_0, K_1, V_0 in LDS; K_2, V_1 staged in registers -------
-  fetch_tile(kh, stage_k, 0, true);
-  fetch_tile(vh, stage_v, 0, false);
-  store_tile(stage_k, lds_k);
-  store_tile(stage_v, lds_v);
-  if (n_tiles > 1) {
-    fetch_tile(kh, stage_k, 1, true);
-    store_tile(stage_k, lds_k + G::kTileBytes);
-  }
-  if (n_tiles > 2) fetch_tile(kh, stage_k, 2, true);
-  if (n_tiles > 1) fetch_tile(vh, stage_v, 1, false);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pk[kb][h][i] = (__bf16)0.f;
+  using True_ = std::true_type;
+  using False_ = std::false_type;
+  // ---- prologue: K_0, K_1 and V_0 in LDS -----------------------------------
+  copy_tile(kh, 0, 0, True_{});
+  copy_tile(vh, 0, 0, False_{});
+  if (n_tiles > 1) copy_tile(kh, 1, 1, True_{});
+  wait_vmem(0);
   __syncthreads();
 
   // ---- phases ----------------------------------------------------------------
   // Phase p: group 0 runs the matrix phase of tile p/2 (p even) or the
   // vector phase of tile (p-1)/2 (p odd); group 1 does the same one phase
   // later.  K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3.
-  // At phase 2j (j >= 1) the LDS buffers of K_{j-1} and V_{j-2} are free:
-  // the staged K_{j+1} and V_j are written into them (first read in phase
-  // 2j+2) and K_{j+2}, V_{j+1} are fetched into the staging registers.
-  // Each group runs its own straight-line loop; both pass the same number
-  // of barriers.
-  auto ring = [&](int j) {
-    if (j + 1 < n_tiles) store_tile(stage_k, lds_k + ((j + 1) % kRing) * G::kTileBytes);
-    store_tile(stage_v, lds_v + (j % kRing) * G::kTileBytes);
-    if (j + 2 < n_tiles) fetch_tile(kh, stage_k, j + 2, true);
-    if (j + 1 < n_tiles) fetch_tile(vh, stage_v, j + 1, false);
+  // At phase 2j the ring slots of K_{j-1} and V_{j-2} are dead, so K_{j+2}
+  // and V_{j+1} are copied into them; both are first read in phase 2j+4.
+  // Before the barrier that ends phase 2j+1 each wave waits for its copies
+  // issued at phase 2j-2, leaving the ones issued at phase 2j in flight.
+  // Each group runs its own straight-line loop (unrolled by three for the
+  // ring slot); both pass the same number of barriers.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  auto issue = [&](int j, auto slot) __attribute__((always_inline)) {  // slot = j % 3
+    constexpr int S = decltype(slot)::value;
+    if (j + 2 < n_tiles) copy_tile(kh, (S + 2) % kRing, j + 2, True_{});
+    if (j + 1 < n_tiles) copy_tile(vh, (S + 1) % kRing, j + 1, False_{});
+  };
+  // copies issued at phase 2j (what may stay in flight at the end of 2j+1)
+  auto in_flight = [&](int j) __attribute__((always_inline)) {
+    return (j + 2 < n_tiles ? n_copy_k : 0) + (j + 1 < n_tiles ? n_copy_v : 0);
+  };
+  // Tile 0 has no previous P*V: its matrix phase computes scores only.
+  auto first_matrix_phase = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    scores_mfma(lds_k);
+    sched_reads_ahead<2 * G::kKSteps, 1>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto last_pv = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    switch ((n_tiles - 1) % kRing) {
+      case 0: pv_mfma(lds_v); break;
+      case 1: pv_mfma(lds_v + G::kTileV); break;
+      default: pv_mfma(lds_v + 2 * G::kTileV); break;
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
   if (grp == 0) {
-    for (int j = 0; j < n_tiles; ++j) {
-      if (j >= 1) ring(j);
-      matrix_phase(j);
+    auto step = [&](int j, auto slot) __attribute__((always_inline)) {
+      issue(j, slot);
+      matrix_phase(slot);
       __syncthreads();
       vector_phase(j);
+      wait_vmem(in_flight(j));
       __syncthreads();
+    };
+    issue(0, S0{});
+    first_matrix_phase();
+    __syncthreads();
+    vector_phase(0);
+    wait_vmem(in_flight(0));
+    __syncthreads();
+    int j = 1;
+    for (; j + 2 < n_tiles; j += 3) {
+      step(j, S1{});
+      step(j + 1, S2{});
+      step(j + 2, S0{});
     }
-    __builtin_amdgcn_s_setprio(1);
-    pv_mfma(n_tiles - 1);
-    __builtin_amdgcn_s_setprio(0);
+    if (j < n_tiles) step(j, S1{});
+    if (j + 1 < n_tiles) step(j + 1, S2{});
+    last_pv();
     __syncthreads();
     __syncthreads();
   } else {
-    __syncthreads();
-    matrix_phase(0);
-    __syncthreads();
-    for (int j = 1; j < n_tiles; ++j) {
-      ring(j);
+    auto step = [&](int j, auto slot) __attribute__((always_inline)) {
+      issue(j, slot);
       vector_phase(j - 1);
       __syncthreads();
-      matrix_phase(j);
+      matrix_phase(slot);
+      wait_vmem(in_flight(j));
       __syncthreads();
+    };
+    issue(0, S0{});
+    __syncthreads();
+    first_matrix_phase();
+    wait_vmem(in_flight(0));
+    __syncthreads();
+    int j = 1;
+    for (; j + 2 < n_tiles; j += 3) {
+      step(j, S1{});
+      step(j + 1, S2{});
+      step(j + 2, S0{});
     }
+    if (j < n_tiles) step(j, S1{});
+    if (j + 1 < n_tiles) step(j + 1, S2{});
     vector_phase(n_tiles - 1);
     __syncthreads();
-    __builtin_amdgcn_s_setprio(1);
-    pv_mfma(n_tiles - 1);
-    __builtin_amdgcn_s_setprio(0);
+    last_pv();
     __syncthreads();
   }
 
