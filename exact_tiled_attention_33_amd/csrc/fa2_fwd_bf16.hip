@@ -11,10 +11,10 @@
 // Per key tile j a wavefront computes the transposed score tile
 //     S^T (64 keys x 32 queries) = K_j * Q^T
 // with v_mfma_f32_32x32x16_bf16, so that each lane holds scores of ONE query
-// (lane % 32) for 32 of the 64 keys: row reductions are in-lane plus one
-// exchange between the two 32-lane halves (v_permlane32_swap).  The
-// probabilities stay in registers in the layout the second product needs as
-// its B operand:
+// (lane % 32) for 32 of the 64 keys: the row max and row sum are in-lane
+// reductions plus one exchange between the two 32-lane halves
+// (v_permlane32_swap).  The probabilities stay in registers in the layout the
+// second product needs as its B operand:
 //     O^T (d x 32 queries) += V_j^T * P^T
 // with the key index (the contraction) relabelled to match the score
 // accumulator, and the V^T operands read straight from the row-major V tile
@@ -26,26 +26,24 @@
 // denominator l and an unnormalised accumulator.  With c = scale*log2(e):
 //     P   = exp2(S*c - m*c)          (one FMA + one v_exp_f32 per score)
 //     l  += rowsum P;  O^T += V^T P^T
-// m is moved (and l and O^T multiplied by exp2((m_old - m_new)*c), the
-// correction that keeps the result exact) only when the probabilities
-// against the current m would grow past a bound; the division by l happens
-// once, when the query tile is finished (Saraf section 2.2).  Causal key
-// tiles entirely above a wavefront's rows are neither multiplied nor (when
-// above the whole workgroup's rows) loaded; only the tile crossing the
-// diagonal, or the ragged end of the sequence, is masked.
+// and when a tile's row max exceeds m by more than a threshold, m moves up
+// and l and O^T are first multiplied by exp2((m_old - m_new)*c) -- the
+// correction that keeps the result exact.  The division by l happens once,
+// when the query tile is finished (Saraf section 2.2).  Causal key tiles
+// entirely above the diagonal are never loaded or multiplied; only tiles
+// crossing the diagonal (or the ragged end of the sequence) are masked.
 //
-// Schedule (where gfx950 differs from the pages' A100 design): the vector
-// work of the softmax costs about a third of the matrix work of a tile, and
-// one wavefront alone issues vector instructions at only about half the
-// SIMD's rate, so every wavefront runs a software pipeline that keeps both
-// kinds of work in one instruction stream: while it computes the
-// probabilities of tile j, its matrix core computes S of tile j+1 and
-// O += V P of tile j-1, with three or four vector instructions issued
-// between consecutive MFMAs.  The two wavefronts of a SIMD run the same
-// pipeline and share its matrix core.  K/V tiles are copied from global
-// memory straight into 3-deep (padded) LDS rings two iterations before
-// they are read; one workgroup barrier per iteration publishes the copies
-// and frees the ring slots.
+// Schedule on the SIMD (this is where gfx950 differs from the pages' A100
+// design): the scalar work of the softmax costs about as many cycles as the
+// matrix work of a tile, so the two must overlap.  The 8 wavefronts form two
+// groups of 4, and wavefront w shares its SIMD with wavefront w + 4.  Time
+// is cut into phases separated by workgroup barriers; group 1 runs one phase
+// behind group 0.  In every phase one group is in a matrix phase (S of tile
+// j, then O += V P of tile j-1: 32 MFMAs) while the other is in a vector
+// phase (mask, row max, correction, exp2, row sum, bf16 packing of tile j),
+// so each SIMD always has MFMA and VALU work from different wavefronts.
+// K/V tiles are copied from global memory straight into 3-deep (padded) LDS
+// rings four phases before they are first read, and read by both groups.
 
 #include "fa2_launch.h"
 
@@ -66,7 +64,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int kWaves = kBf16Waves;      // 8, two per SIMD
+constexpr int kWaves = kBf16Waves;      // 8: two groups of 4
+constexpr int kGroupWaves = kWaves / 2;
 constexpr int kRows = 32;               // query rows per wavefront
 constexpr int kBr = kBf16BlockRows;     // query rows per workgroup
 constexpr int kBc = kBf16BlockCols;     // keys per K/V tile
@@ -126,7 +125,23 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 constexpr int kAhead = 4;  // LDS operand reads in flight ahead of the MFMAs
+
+// Schedule n_mfma MFMAs, each needing `reads` LDS reads, so that the reads
+// run kAhead MFMAs ahead of their consumer.
+template <int kNMfma, int kReads>
+__device__ __forceinline__ void sched_reads_ahead() {
+#pragma unroll
+  for (int n = 0; n < kAhead; ++n) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+#pragma unroll
+  for (int n = 0; n < kNMfma; ++n) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (n + kAhead < kNMfma) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+  }
+}
 
 // Raw buffer descriptor as four scalar registers, for the LDS copy below.
 __device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
@@ -171,6 +186,16 @@ __device__ __forceinline__ void wait_vmem(int n) {
   }
 }
 
+// Pins a value to this point of the instruction stream.  asm volatile
+// statements keep their order relative to the workgroup barriers, so this
+// stops the compiler from moving the vector work of a phase (pure register
+// arithmetic) across the barriers that delimit the phase.
+template <typename T>
+__device__ __forceinline__ T pin(T x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Lazy max correction: the reference max m of a row is only moved (and the
 // banked l and O corrected) when a tile's row max exceeds it by more than
 // this many powers of two, so the unnormalised probabilities stay in
@@ -180,42 +205,23 @@ __device__ __forceinline__ void wait_vmem(int n) {
 // keeps the answer exact.
 constexpr float kRescaleThreshold = 32.0f;
 
-typedef const __attribute__((address_space(3))) char* lds_cptr;
-
-// Hides x from the optimiser, so that a per-stage LDS base stays one
-// register and every operand read of the stage is that register plus an
-// immediate offset (rather than one register per read, hoisted out of the
-// key loop).
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-// Pins a value to this point of the instruction stream: the vector work of
-// a pipeline stage must neither be hoisted above the barrier that starts
-// the stage nor sunk below its MFMAs, or it would no longer interleave with
-// them.  (asm volatile statements keep their order relative to barriers.)
-template <typename T>
-__device__ __forceinline__ T pin(T x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int T, float c) {
   using G = Geo<D>;
-  constexpr int kNPv = 4 * G::kDBlocks;  // MFMAs of O^T += V^T P^T per tile
-  constexpr int kNS = 2 * G::kKSteps;    // MFMAs of S^T = K Q^T per tile
-  // K ring (3 tiles) then V ring (3 tiles)
+  // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
+  char* const lds_k = smem;
+  char* const lds_v = smem + kRing * G::kTileK;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform values are made explicit so they live in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / kGroupWaves;  // 0 or 1 (group 1 runs one phase behind)
+  const int gw = wave % kGroupWaves;   // position within the group = SIMD
   const int l32 = lane & 31;           // query column of this lane
   const int half = lane >> 5;          // which 4-key sub-rows of each 8-key group
 
@@ -229,9 +235,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const __bf16* kh = k + head;
   const __bf16* vh = v + head;
 
+  // Rows: the two wavefronts of a SIMD take adjacent 32-row slices, so the
+  // causal work of the two groups stays balanced.
   const int q0 = t * kBr;
-  const int qw = q0 + kRows * wave;  // first row of this wavefront
-  const int qrow = qw + l32;         // this lane's query row
+  const int qw = q0 + 64 * gw + 32 * grp;  // first row of this wavefront
+  const int qrow = qw + l32;               // this lane's query row
 
   // Q rows of the wavefront as MFMA B operands (query = lane % 32,
   // head-dim slice 16*s + 8*half .. +7), held for the whole key loop.
@@ -245,11 +253,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (l32 * D + 16 * s + 8 * half) * 2));
   }
 
-  // Key tiles: the workgroup streams n_tiles of them; this wavefront
-  // multiplies the first n_w (causal: those starting at or below its last
-  // row) and masks those from n_full on.  Because a wavefront's 32 rows
-  // start at a multiple of 32, n_full >= n_w - 1: only its last tile can
-  // need the mask.
+  // Key tiles: the workgroup streams n_tiles of them; this wavefront computes
+  // on the first n_w (causal: those starting at or below its last row) and
+  // masks the ones from n_full on (crossing its diagonal, or the ragged end).
   const int nk = (N + kBc - 1) / kBc;
   int n_tiles = nk, n_w = (qw < N) ? nk : 0, n_full = N / kBc;
   if (CAUSAL) {
@@ -257,7 +263,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     n_w = (qw < N) ? min(nk, (min(qw + kRows, N) - 1) / kBc + 1) : 0;
     n_full = min(n_full, (qw + 1) / kBc);
   }
-  const bool mask_last = n_full < n_w;
 
   // Tile copies: instruction i of a tile fills LDS slots [64i, 64i + 64);
   // slot u is (row u / slots-per-row, chunk u % slots-per-row), and the
@@ -280,16 +285,15 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int chunk = u % G::kSlotsV;
     voff_v[k] = (u / G::kSlotsV) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
   }
-  // LDS byte offsets of the two rings
-  const unsigned lds_k = __builtin_amdgcn_readfirstlane(lds_offset_of(smem));
-  const unsigned lds_v = lds_k + kRing * G::kTileK;
+  const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
+  const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
   auto copy_tile = [&](const __bf16* src, int slot, int j, auto is_k) __attribute__((always_inline)) {
     constexpr bool K_TILE = decltype(is_k)::value;
     constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
     constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
     const int key0 = j * kBc;
     const i32x4 r = raw_rsrc(src + (long long)key0 * D, min(kBc, N - key0) * G::kRowBytes);
-    const unsigned base = (K_TILE ? lds_k + slot * G::kTileK : lds_v + slot * G::kTileV) + wave * 1024;
+    const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
 #pragma unroll
     for (int k = 0; k < kCopy; ++k) {
       if (wave + k * kWaves < kInst)
@@ -300,275 +304,246 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int n_copy_k = (G::kInstK - wave + kWaves - 1) / kWaves;
   const int n_copy_v = (G::kInstV - wave + kWaves - 1) / kWaves;
 
-  // Per-lane LDS offsets within a tile; the rest of every operand address
-  // is an immediate.  K operand (kb, s): row 32*kb + l32, columns
-  // 16*s + 8*half .. +7.  V transposing read for (db, kb, h, u): lane i of
-  // each 16-lane group points at key row (i / 4) of a 4-row slab and dcol
-  // 4*(i % 4) of a 16-column slab; lane i then receives the 4 keys of one
-  // dcol (lane % 32).
+  // Per-lane LDS offsets; everything else is an immediate.  K operand
+  // (kb, s): row 32*kb + l32, columns 16*s + 8*half .. +7.  V transposing
+  // read for (db, kb, h, u): lane i of each 16-lane group points at key row
+  // (i / 4) of a 4-row slab and dcol 4*(i % 4) of a 16-column slab; lane i
+  // then receives the 4 keys of one dcol (lane % 32).
   const int k_lane = l32 * G::kStrideK + 16 * half;
   const int v_lane = (4 * half + ((lane & 15) >> 2)) * G::kStrideV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  // operand bases of key tile j (ring slot j % 3)
-  auto kbase_of = [&](int j) __attribute__((always_inline)) { return opaque(k_lane + (int)(lds_k + (j % kRing) * G::kTileK)); };
-  auto vbase_of = [&](int j) __attribute__((always_inline)) { return opaque(v_lane + (int)(lds_v + (j % kRing) * G::kTileV)); };
+  auto k_off = [&](int kb, int s) __attribute__((always_inline)) { return k_lane + 32 * kb * G::kStrideK + 32 * s; };
+  auto v_off = [&](int db, int kb, int h, int u) __attribute__((always_inline)) { return v_lane + (32 * kb + 16 * h + 8 * u) * G::kStrideV + 64 * db; };
 
   f32x16 oacc[G::kDBlocks];
 #pragma unroll
   for (int db = 0; db < G::kDBlocks; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  // Two score tiles and two packed probability tiles: while the
-  // probabilities of tile j are formed from sacc[j % 2] into pk[j % 2], the
-  // matrix core writes S_{j+1} into sacc[(j + 1) % 2] and reads P_{j-1}
-  // from pk[(j - 1) % 2].
-  f32x16 sacc[2][2];
-  bf16x8 pk[2][2][2];
+  f32x16 sacc[2];
+  bf16x8 pk[2][2];
   float m = -1e30f;  // reference max of raw scores (finite start)
   float l = 0.f;     // running denominator over this lane's keys
 
-  // ---- one pipeline stage --------------------------------------------------
-  // NPV MFMAs of O^T += V^T P^T (V^T from the tile at vbase, P^T from
-  // pk[PB]), then NS MFMAs of S^T = K Q^T (K from the tile at kbase, into
-  // sacc[SB]).  If PROBS, the softmax step of score tile sacc[XB] runs
-  // between the MFMAs: the row max (four chains), the lazy move of m (see
-  // kRescaleThreshold), and per score one FMA, one exp2 and one add (plus
-  // one bf16 pack per pair) into pk[XB], software-pipelined three deep so
-  // that no instruction waits on the one before it.  Each MFMA step is
-  // fenced, so this interleave is the one the hardware sees.  Operands are
-  // read from LDS kAhead MFMAs ahead of their use.  Returns this lane's sum
-  // of the tile's probabilities, the factor alpha that l and O^T must be
-  // multiplied by, and whether m moved anywhere in the wave.
-  struct StageOut { float rs, alpha; bool moved; };
-  auto stage = [&](auto npv_c, auto ns_c, auto probs_c, auto pb_c, auto sb_c, auto xb_c,
-                   int kbase, int vbase) __attribute__((always_inline)) {
-    constexpr int NPV = decltype(npv_c)::value;
-    constexpr int NS = decltype(ns_c)::value;
-    constexpr bool PROBS = decltype(probs_c)::value;
-    constexpr int PB = decltype(pb_c)::value, SB = decltype(sb_c)::value, XB = decltype(xb_c)::value;
-    constexpr int kSteps = NPV + NS;
-    // steps that reduce the row max, then steps that start the 32 scores
-    constexpr int kMaxSteps = kSteps >= 32 ? 4 : 2;
-    constexpr int kElSteps = kSteps > kMaxSteps ? kSteps - kMaxSteps : 1;
-    // scores whose FMA is issued at step n: [e_lo(n), e_lo(n + 1))
-    auto e_lo = [](int n) {
-      const int k = n - kMaxSteps;
-      return k <= 0 ? 0 : k >= kElSteps ? 32 : (32 * k + kElSteps - 1) / kElSteps;
-    };
-    constexpr int kLastStep = (kSteps > kMaxSteps ? kSteps : kMaxSteps + 1) + 1;  // last A step
-    auto read = [&](int n) __attribute__((always_inline)) {
-      if (n < NPV) {
-        // MFMA n: O^T block n % kDBlocks, key step n / kDBlocks = (kb, h);
-        // operand slot u of lane (l32, half) is key 8*(u/4) + 4*half + (u%4)
-        // in both the P^T operand (accumulator elements 8h..8h+7) and V^T.
-        const int db = n % G::kDBlocks, ks = n / G::kDBlocks;
-        const int off = (32 * (ks >> 1) + 16 * (ks & 1)) * G::kStrideV + 64 * db;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_cptr)(size_t)(vbase + off));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lds_cptr)(size_t)(vbase + off + 8 * G::kStrideV));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      // MFMA NPV + s: score block s % 2 (two independent chains), k-step s / 2
-      const int s = n - NPV;
-      return *(const __attribute__((address_space(3))) bf16x8*)(lds_cptr)(size_t)(kbase + 32 * (s & 1) * G::kStrideK + 32 * (s >> 1));
-    };
-    auto mfma = [&](int n, const bf16x8& a) __attribute__((always_inline)) {
-      if (n < NPV) {
-        const int db = n % G::kDBlocks, ks = n / G::kDBlocks;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[PB][ks >> 1][ks & 1], oacc[db], 0, 0, 0);
-      } else {
-        const int s = n - NPV, kb = s & 1, ks = s >> 1;
-        sacc[SB][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : sacc[SB][kb], 0, 0, 0);
-      }
-    };
-    // softmax state
-    float mx[4], mc = 0.f, alpha = 1.f;
-    bool moved = false;
-    float t[32], p[32];
-    u32x4 w[2][2];
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    auto score = [&](int e) __attribute__((always_inline)) { return sacc[XB][e >> 4][e & 15]; };
-    auto max_part = [&](int g) __attribute__((always_inline)) {  // scores [32g/kMaxSteps, 32(g+1)/kMaxSteps)
+  // ---- matrix phase of tile j: S_j = K_j Q^T, then O^T += V_{j-1}^T P_{j-1}^T
+  // No branches here: for tiles past a wavefront's last row the scores are
+  // computed but fully masked in the vector phase, so their P is 0.
+  // Operands are read from LDS kAhead MFMAs ahead of their use.
+  auto scores_mfma = [&](const char* kbuf) __attribute__((always_inline)) {
+    // MFMA n uses k-step s = n / 2 of block kb = n % 2 (two independent chains).
+    constexpr int kN = 2 * G::kKSteps;
+    auto read_k = [&](int n) __attribute__((always_inline)) { return *(const bf16x8*)(kbuf + k_off(n & 1, n >> 1)); };
+    bf16x8 ka[kAhead];
 #pragma unroll
-      for (int e = 32 * g / kMaxSteps; e < 32 * (g + 1) / kMaxSteps; e += 8)
+    for (int n = 0; n < kAhead; ++n) ka[n] = read_k(n);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          mx[r] = (g == 0 && e == 0) ? fmaxf(score(e + r), score(e + r + 4))
-                                     : fmaxf(fmaxf(mx[r], score(e + r)), score(e + r + 4));
+    for (int n = 0; n < kN; ++n) {
+      const bf16x8 a = ka[n % kAhead];
+      if (n + kAhead < kN) ka[n % kAhead] = read_k(n + kAhead);
+      sacc[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n >> 1], n < 2 ? f32x16{} : sacc[n & 1], 0, 0, 0);
+    }
+  };
+  auto pv_mfma = [&](const char* vbuf) __attribute__((always_inline)) {
+    // Key step (kb, h) covers keys 32*kb + 16*h + {0..15}; operand slot u
+    // of lane (l32, half) is key 8*(u/4) + 4*half + (u%4) in both the P^T
+    // operand (accumulator elements 8h..8h+7) and the V^T one.  MFMA n uses
+    // key step n / kDBlocks on O^T block n % kDBlocks.
+    constexpr int kN = 4 * G::kDBlocks;
+    auto read_v = [&](int n, bf16x4 (&dst)[2]) {
+      const int db = n % G::kDBlocks, kb = (n / G::kDBlocks) >> 1, h = (n / G::kDBlocks) & 1;
+      dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbuf + v_off(db, kb, h, 0)));
+      dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbuf + v_off(db, kb, h, 1)));
     };
-    auto decide = [&]() __attribute__((always_inline)) {
-      const float mt = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-      moved = __builtin_amdgcn_ballot_w64((mt - m) * c > kRescaleThreshold) != 0;
-      const float m_new = moved ? fmaxf(m, mt) : m;
-      alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+    bf16x4 va[kAhead][2];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) read_v(n, va[n]);
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      const bf16x8 a = __builtin_shufflevector(va[n % kAhead][0], va[n % kAhead][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      if (n + kAhead < kN) read_v(n + kAhead, va[n % kAhead]);
+      const int db = n % G::kDBlocks, ks = n / G::kDBlocks;
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
+    }
+  };
+  // Tile j's K is in ring slot j % 3, tile j-1's V in slot (j - 1) % 3; the
+  // slot is a compile-time constant in each third of the unrolled loops
+  // below, so every LDS address is a base register plus an immediate.
+  auto matrix_phase = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    __builtin_amdgcn_s_setprio(1);
+    scores_mfma(lds_k + S * G::kTileK);
+    pv_mfma(lds_v + ((S + kRing - 1) % kRing) * G::kTileV);
+    // Keep each operand read kAhead MFMAs ahead of its use: LDS latency
+    // (~70 cycles unloaded) exceeds one MFMA (32 cycles).
+    sched_reads_ahead<2 * G::kKSteps, 1>();
+    sched_reads_ahead<4 * G::kDBlocks, 2>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- vector phase of tile j: mask, row max, correction, P = exp2(...) ----
+  auto vector_phase = [&](int j) __attribute__((always_inline)) {
+    if (j >= n_full) {
+      // element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*half + (i%4);
+      // tiles at or past n_w lie wholly above this wave's rows -> all masked
+      const int key0 = j * kBc;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          const bool vis = (key < N) && (!CAUSAL || key <= qrow);
+          if (!vis) sacc[kb][i] = -INFINITY;
+        }
+    }
+    sacc[0] = pin(sacc[0]);
+    sacc[1] = pin(sacc[1]);
+    // Row max in four independent chains (chain r takes the elements
+    // e = 16*kb + i with e % 4 == r), then both halves of the row.
+    auto el = [&](int e) __attribute__((always_inline)) { return sacc[e >> 4][e & 15]; };
+    float mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx[r] = fmaxf(el(r), el(r + 4));
+#pragma unroll
+    for (int e = 8; e < 32; e += 8)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx[r] = fmaxf(fmaxf(mx[r], el(e + r)), el(e + r + 4));
+    const float mt = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+    // Move the reference max only when some row's tile max exceeds it by
+    // more than the threshold; then correct the banked terms.  The first
+    // tile always moves it (m starts at -1e30) unless c is vanishingly
+    // small, in which case every probability is 1 and m never matters.
+    if (__builtin_amdgcn_ballot_w64((mt - m) * c > kRescaleThreshold)) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
       m = m_new;
-      mc = pin(m * c);
-    };
-    // (each result is pinned where it is computed: without that, the
-    // instruction selector is free to gather all of them after the MFMAs)
-    auto op_f = [&](int e) __attribute__((always_inline)) {
-      t[e] = pin(fmaf(score(e), c, -mc));
-    };
-    auto op_x = [&](int e) __attribute__((always_inline)) {
-      p[e] = pin(__builtin_amdgcn_exp2f(t[e]));
-    };
-    auto op_a = [&](int e) __attribute__((always_inline)) {
-      part[e & 3] = pin(part[e & 3] + p[e]);
-      if (e & 1) {
-        const bf16x2 pp = {(__bf16)p[e - 1], (__bf16)p[e]};
-        const int kb = e >> 4, i = e & 15;
-        w[kb][i >> 3][(i & 7) >> 1] = pin(__builtin_bit_cast(unsigned, pp));
-      }
-    };
-    auto valu_of_step = [&](int n) __attribute__((always_inline)) {
-      if (n < kMaxSteps) max_part(n);
-      if (n == kMaxSteps - 1) decide();
-#pragma unroll
-      for (int e = e_lo(n - 2); e < e_lo(n - 1); ++e) op_a(e);
-#pragma unroll
-      for (int e = e_lo(n - 1); e < e_lo(n); ++e) op_x(e);
-#pragma unroll
-      for (int e = e_lo(n); e < e_lo(n + 1); ++e) op_f(e);
-    };
-
-    bf16x8 op[kAhead];
-#pragma unroll
-    for (int n = 0; n < kAhead && n < kSteps; ++n) op[n] = read(n);
-#pragma unroll
-    for (int n = 0; n < kSteps; ++n) {
-      const bf16x8 a = op[n % kAhead];
-      if (n + kAhead < kSteps) op[n % kAhead] = read(n + kAhead);
-      mfma(n, a);
-      if (PROBS) valu_of_step(n);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (PROBS) {
-      // drain the pipeline (and, without MFMAs, run the whole softmax step)
-#pragma unroll
-      for (int n = kSteps; n <= kLastStep; ++n) valu_of_step(n);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pk[XB][kb][0] = __builtin_bit_cast(bf16x8, w[kb][0]);
-        pk[XB][kb][1] = __builtin_bit_cast(bf16x8, w[kb][1]);
-      }
-    }
-    StageOut r{(part[0] + part[1]) + (part[2] + part[3]), alpha, moved};
-    return r;
-  };
-
-  // Mask of the scores of tile j (keys past N; causal: keys after the row).
-  // Element i of block kb holds key 64*j + 32*kb + 8*(i/4) + 4*half + (i%4).
-  auto apply_mask = [&](auto xb_c, int j) __attribute__((always_inline)) {
-    constexpr int XB = decltype(xb_c)::value;
-    const int key0 = j * kBc;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-        const bool vis = (key < N) && (!CAUSAL || key <= qrow);
-        if (!vis) sacc[XB][kb][i] = -INFINITY;
-      }
-  };
-  // l and O^T banked against the old m are moved to the new one (O^T after
-  // the stage's own MFMAs into it; the branch is taken only when m moved).
-  auto bank = [&](const StageOut& r) __attribute__((always_inline)) {
-    l = fmaf(l, r.alpha, r.rs);
-    if (r.moved) {
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < G::kDBlocks; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= r.alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-  };
-  using Z = std::integral_constant<int, 0>;
-  using O = std::integral_constant<int, 1>;
-  using PvN = std::integral_constant<int, kNPv>;
-  using SN = std::integral_constant<int, kNS>;
-  using Yes = std::true_type;
-  using No = std::false_type;
-
-  // ---- iterations ------------------------------------------------------------
-  // Iteration it reads K_{it+1} (for S_{it+1}) and V_{it-1} (for P_{it-1} V).
-  // It starts with a workgroup barrier: every wave has finished iteration
-  // it-1, so the ring slots of K_it and V_{it-2} are free, and (each wave
-  // having first waited for its own copies issued up to iteration it-2)
-  // K_{it+1} and V_{it-1} have landed.  After the barrier the wave copies
-  // K_{it+3} and V_{it+1} into the free slots.  The prologue provides K_0,
-  // K_1, K_2 and V_0.  Every wave runs n_tiles + 1 iterations; it computes
-  // in iterations 0 .. n_w and only takes part in the barriers and copies
-  // after that.
-  auto issue = [&](int it) __attribute__((always_inline)) {
-    if (it + 3 < n_tiles) copy_tile(kh, it % kRing, it + 3, Yes{});
-    if (it + 1 < n_tiles) copy_tile(vh, (it + 1) % kRing, it + 1, No{});
-  };
-  auto in_flight = [&](int it) __attribute__((always_inline)) {
-    return (it + 3 < n_tiles ? n_copy_k : 0) + (it + 1 < n_tiles ? n_copy_v : 0);
-  };
-  auto sync = [&](int it) __attribute__((always_inline)) {
-    if (it >= 1) wait_vmem(in_flight(it - 1));
-    __syncthreads();
-    issue(it);
+    // P = exp2(S*c - m*c), rounded to bf16 in pairs into the P^T operand;
+    // the row sum adds the unrounded values in four independent chains.
+    // Masked scores are -inf and c > 0, so their probability is exactly 0.
+    const float mc = m * c;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 w[2];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, -mc));
+        part[i & 3] += p0;
+        part[(i & 3) + 1] += p1;
+        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+        w[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(unsigned, pp);
+      }
+      pk[kb][0] = pin(__builtin_bit_cast(bf16x8, w[0]));
+      pk[kb][1] = pin(__builtin_bit_cast(bf16x8, w[1]));
+    }
+    l = pin(l + ((part[0] + part[1]) + (part[2] + part[3])));
   };
 
-  // ---- prologue ----------------------------------------------------------------
-  copy_tile(kh, 0, 0, Yes{});
-  copy_tile(vh, 0, 0, No{});
-  if (n_tiles > 1) copy_tile(kh, 1, 1, Yes{});
-  if (n_tiles > 2) copy_tile(kh, 2, 2, Yes{});
+  using True_ = std::true_type;
+  using False_ = std::false_type;
+  // ---- prologue: K_0, K_1 and V_0 in LDS -----------------------------------
+  copy_tile(kh, 0, 0, True_{});
+  copy_tile(vh, 0, 0, False_{});
+  if (n_tiles > 1) copy_tile(kh, 1, 1, True_{});
   wait_vmem(0);
   __syncthreads();
 
-  int it = 0;
-  if (n_w >= 1) {
-    stage(Z{}, SN{}, No{}, Z{}, Z{}, Z{}, kbase_of(0), 0);  // S_0
-    sync(0);
-    // tile 0 (m starts at -1e30, so the first softmax step always moves it;
-    // nothing is banked yet, so alpha = 0 is harmless)
-    if (n_w == 1) {
-      if (mask_last) apply_mask(Z{}, 0);
-      bank(stage(Z{}, Z{}, Yes{}, Z{}, Z{}, Z{}, 0, 0));
-    } else {
-      bank(stage(Z{}, SN{}, Yes{}, Z{}, O{}, Z{}, kbase_of(1), 0));
+  // ---- phases ----------------------------------------------------------------
+  // Phase p: group 0 runs the matrix phase of tile p/2 (p even) or the
+  // vector phase of tile (p-1)/2 (p odd); group 1 does the same one phase
+  // later.  K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3.
+  // At phase 2j the ring slots of K_{j-1} and V_{j-2} are dead, so K_{j+2}
+  // and V_{j+1} are copied into them; both are first read in phase 2j+4.
+  // Before the barrier that ends phase 2j+1 each wave waits for its copies
+  // issued at phase 2j-2, leaving the ones issued at phase 2j in flight.
+  // Each group runs its own straight-line loop (unrolled by three for the
+  // ring slot); both pass the same number of barriers.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  auto issue = [&](int j, auto slot) __attribute__((always_inline)) {  // slot = j % 3
+    constexpr int S = decltype(slot)::value;
+    if (j + 2 < n_tiles) copy_tile(kh, (S + 2) % kRing, j + 2, True_{});
+    if (j + 1 < n_tiles) copy_tile(vh, (S + 1) % kRing, j + 1, False_{});
+  };
+  // copies issued at phase 2j (what may stay in flight at the end of 2j+1)
+  auto in_flight = [&](int j) __attribute__((always_inline)) {
+    return (j + 2 < n_tiles ? n_copy_k : 0) + (j + 1 < n_tiles ? n_copy_v : 0);
+  };
+  // Tile 0 has no previous P*V: its matrix phase computes scores only.
+  auto first_matrix_phase = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    scores_mfma(lds_k);
+    sched_reads_ahead<2 * G::kKSteps, 1>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto last_pv = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    switch ((n_tiles - 1) % kRing) {
+      case 0: pv_mfma(lds_v); break;
+      case 1: pv_mfma(lds_v + G::kTileV); break;
+      default: pv_mfma(lds_v + 2 * G::kTileV); break;
     }
-    it = 1;
-    // steady state: P_{j-1} V, softmax step of tile j, S_{j+1}
-    auto steady = [&](int j, auto xb_c) __attribute__((always_inline)) {
-      constexpr int X = decltype(xb_c)::value;
-      using Xc = std::integral_constant<int, X>;
-      using Yc = std::integral_constant<int, 1 - X>;
-      sync(j);
-      bank(stage(PvN{}, SN{}, Yes{}, Yc{}, Yc{}, Xc{}, kbase_of(j + 1), vbase_of(j - 1)));
+    __builtin_amdgcn_s_setprio(0);
+  };
+  if (grp == 0) {
+    auto step = [&](int j, auto slot) __attribute__((always_inline)) {
+      issue(j, slot);
+      matrix_phase(slot);
+      __syncthreads();
+      vector_phase(j);
+      wait_vmem(in_flight(j));
+      __syncthreads();
     };
-    for (; it + 1 <= n_w - 2; it += 2) {
-      steady(it, O{});
-      steady(it + 1, Z{});
+    issue(0, S0{});
+    first_matrix_phase();
+    __syncthreads();
+    vector_phase(0);
+    wait_vmem(in_flight(0));
+    __syncthreads();
+    int j = 1;
+    for (; j + 2 < n_tiles; j += 3) {
+      step(j, S1{});
+      step(j + 1, S2{});
+      step(j + 2, S0{});
     }
-    if (it <= n_w - 2) {
-      steady(it, O{});
-      ++it;
-    }
-    // last tile of this wave (it = n_w - 1 >= 1): P_{it-1} V and its softmax step
-    auto last = [&](int j, auto xb_c) __attribute__((always_inline)) {
-      constexpr int X = decltype(xb_c)::value;
-      using Xc = std::integral_constant<int, X>;
-      using Yc = std::integral_constant<int, 1 - X>;
-      sync(j);
-      if (mask_last) apply_mask(Xc{}, j);
-      bank(stage(PvN{}, Z{}, Yes{}, Yc{}, Z{}, Xc{}, 0, vbase_of(j - 1)));
+    if (j < n_tiles) step(j, S1{});
+    if (j + 1 < n_tiles) step(j + 1, S2{});
+    last_pv();
+    __syncthreads();
+    __syncthreads();
+  } else {
+    auto step = [&](int j, auto slot) __attribute__((always_inline)) {
+      issue(j, slot);
+      vector_phase(j - 1);
+      __syncthreads();
+      matrix_phase(slot);
+      wait_vmem(in_flight(j));
+      __syncthreads();
     };
-    if (n_w >= 2) {
-      if (it & 1) last(it, O{});
-      else last(it, Z{});
-      ++it;
+    issue(0, S0{});
+    __syncthreads();
+    first_matrix_phase();
+    wait_vmem(in_flight(0));
+    __syncthreads();
+    int j = 1;
+    for (; j + 2 < n_tiles; j += 3) {
+      step(j, S1{});
+      step(j + 1, S2{});
+      step(j + 2, S0{});
     }
-    // it = n_w: P_{n_w - 1} V
-    sync(it);
-    if ((n_w - 1) & 1)
-      stage(PvN{}, Z{}, No{}, O{}, Z{}, Z{}, 0, vbase_of(it - 1));
-    else
-      stage(PvN{}, Z{}, No{}, Z{}, Z{}, Z{}, 0, vbase_of(it - 1));
-    ++it;
+    if (j < n_tiles) step(j, S1{});
+    if (j + 1 < n_tiles) step(j + 1, S2{});
+    vector_phase(n_tiles - 1);
+    __syncthreads();
+    last_pv();
+    __syncthreads();
   }
-  for (; it <= n_tiles; ++it) sync(it);
 
   // ---- finalise: one division per row, then O and LSE ----------------------
   const float lt = sum_halves(l);
