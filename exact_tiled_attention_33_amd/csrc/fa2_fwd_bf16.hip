@@ -130,6 +130,13 @@ constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 constexpr int kAhead = 4;  // LDS operand reads in flight ahead of the MFMAs
 
+// sched_group_barrier takes constant arguments only; this maps a read count
+// that is constant after unrolling onto one of them.
+__device__ __forceinline__ void sched_ds_reads(int n) {
+  if (n == 1) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  else __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+}
+
 // Schedule n_mfma MFMAs, each needing `reads` LDS reads, so that the reads
 // run kAhead MFMAs ahead of their consumer.
 template <int kNMfma, int kReads>
@@ -366,16 +373,51 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   };
   // Tile j's K is in ring slot j % 3, tile j-1's V in slot (j - 1) % 3; the
   // slot is a compile-time constant in each third of the unrolled loops
-  // below, so every LDS address is a base register plus an immediate.
+  // below, so every LDS address is a base register plus an immediate.  The
+  // 16 MFMAs of S_j and the 16 of O^T += V_{j-1}^T P_{j-1}^T form one stream
+  // whose operand reads run kAhead MFMAs ahead across the boundary between
+  // the two products, so the first O^T MFMA does not wait for a fresh read.
   auto matrix_phase = [&](auto slot) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
+    constexpr int kNS = 2 * G::kKSteps;   // MFMAs of S_j
+    constexpr int kNP = 4 * G::kDBlocks;  // MFMAs of O^T
+    const char* kbuf = lds_k + S * G::kTileK;
+    const char* vbuf = lds_v + ((S + kRing - 1) % kRing) * G::kTileV;
+    // MFMA n < kNS: k-step n / 2 of score block n % 2 (two independent
+    // chains).  MFMA kNS + m: key step m / kDBlocks (= (kb, h), keys
+    // 32*kb + 16*h + {0..15}) on O^T block m % kDBlocks; operand slot u of
+    // lane (l32, half) is key 8*(u/4) + 4*half + (u%4) in both the P^T
+    // operand (accumulator elements 8h..8h+7) and the V^T one.
+    auto read_op = [&](int n) __attribute__((always_inline)) {
+      if (n < kNS) return *(const bf16x8*)(kbuf + k_off(n & 1, n >> 1));
+      const int m = n - kNS, db = m % G::kDBlocks, kb = (m / G::kDBlocks) >> 1, h = (m / G::kDBlocks) & 1;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbuf + v_off(db, kb, h, 0)));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbuf + v_off(db, kb, h, 1)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
     __builtin_amdgcn_s_setprio(1);
-    scores_mfma(lds_k + S * G::kTileK);
-    pv_mfma(lds_v + ((S + kRing - 1) % kRing) * G::kTileV);
-    // Keep each operand read kAhead MFMAs ahead of its use: LDS latency
-    // (~70 cycles unloaded) exceeds one MFMA (32 cycles).
-    sched_reads_ahead<2 * G::kKSteps, 1>();
-    sched_reads_ahead<4 * G::kDBlocks, 2>();
+    bf16x8 op[kAhead];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) op[n] = read_op(n);
+#pragma unroll
+    for (int n = 0; n < kNS + kNP; ++n) {
+      const bf16x8 a = op[n % kAhead];
+      if (n + kAhead < kNS + kNP) op[n % kAhead] = read_op(n + kAhead);
+      if (n < kNS) {
+        sacc[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n >> 1], n < 2 ? f32x16{} : sacc[n & 1], 0, 0, 0);
+      } else {
+        const int m = n - kNS, db = m % G::kDBlocks, ks = m / G::kDBlocks;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
+      }
+    }
+    // each MFMA is preceded by the reads of the MFMA kAhead later
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) sched_ds_reads(n < kNS ? 1 : 2);
+#pragma unroll
+    for (int n = 0; n < kNS + kNP; ++n) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (n + kAhead < kNS + kNP) sched_ds_reads(n + kAhead < kNS ? 1 : 2);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -457,10 +499,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // Phase p: group 0 runs the matrix phase of tile p/2 (p even) or the
   // vector phase of tile (p-1)/2 (p odd); group 1 does the same one phase
   // later.  K_j is read in phases 2j and 2j+1, V_j in phases 2j+2 and 2j+3.
-  // At phase 2j the ring slots of K_{j-1} and V_{j-2} are dead, so K_{j+2}
-  // and V_{j+1} are copied into them; both are first read in phase 2j+4.
-  // Before the barrier that ends phase 2j+1 each wave waits for its copies
-  // issued at phase 2j-2, leaving the ones issued at phase 2j in flight.
+  // From phase 2j on, the ring slots of K_{j-1} and V_{j-2} are dead, so
+  // K_{j+2} and V_{j+1} are copied into them in step j (phase 2j for group
+  // 1, phase 2j+1 for group 0: each group at the start of its vector phase);
+  // both are first read in phase 2j+4.  Before the barrier that ends step j
+  // each wave waits for its copies of step j-1, leaving those of step j in
+  // flight.
   // Each group runs its own straight-line loop (unrolled by three for the
   // ring slot); both pass the same number of barriers.
   using S0 = std::integral_constant<int, 0>;
@@ -471,7 +515,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (j + 2 < n_tiles) copy_tile(kh, (S + 2) % kRing, j + 2, True_{});
     if (j + 1 < n_tiles) copy_tile(vh, (S + 1) % kRing, j + 1, False_{});
   };
-  // copies issued at phase 2j (what may stay in flight at the end of 2j+1)
+  // copies of step j (what may stay in flight at the end of step j)
   auto in_flight = [&](int j) __attribute__((always_inline)) {
     return (j + 2 < n_tiles ? n_copy_k : 0) + (j + 1 < n_tiles ? n_copy_v : 0);
   };
@@ -492,17 +536,20 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __builtin_amdgcn_s_setprio(0);
   };
   if (grp == 0) {
+    // Group 0 issues its copies of step j at the start of its vector phase
+    // (phase 2j+1) rather than of its matrix phase: a copy stalls the wave
+    // that issues it, and the vector phase has the slack.
     auto step = [&](int j, auto slot) __attribute__((always_inline)) {
-      issue(j, slot);
       matrix_phase(slot);
       __syncthreads();
+      issue(j, slot);
       vector_phase(j);
       wait_vmem(in_flight(j));
       __syncthreads();
     };
-    issue(0, S0{});
     first_matrix_phase();
     __syncthreads();
+    issue(0, S0{});
     vector_phase(0);
     wait_vmem(in_flight(0));
     __syncthreads();
