@@ -11,6 +11,8 @@
 
 #include "fa2_launch.h"
 
+#include <cstdlib>
+
 namespace {
 
 bool is_dtype(int x) { return x == FA2_F32 || x == FA2_BF16; }
@@ -129,6 +131,8 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.causal = causal != 0;
   a.scale = scale;
   a.o_bf16 = (o_dtype == FA2_BF16);
+  const char* dbg = std::getenv("FA2_DEBUG_POISON");
+  a.poison = dbg != nullptr && dbg[0] != '\0' && dbg[0] != '0';
   a.stream = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = (in_dtype == FA2_BF16) ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;

@@ -216,7 +216,7 @@ template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
-                     int BH, int N, int T, float c) {
+                     int BH, int N, int T, float c, int poison) {
   using G = Geo<D>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
@@ -301,6 +301,19 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int key0 = j * kBc;
     const i32x4 r = raw_rsrc(src + (long long)key0 * D, min(kBc, N - key0) * G::kRowBytes);
     const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
+    if (poison) {
+      // Debug: NaN over the 1 KiB blocks this wave's copies are about to
+      // fill, completed before the copies are issued.  A read of the slot
+      // before its copy lands, or a copy into a slot still being read,
+      // then shows up as NaN in O.
+      const u32x4 nan4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+#pragma unroll
+      for (int k = 0; k < kCopy; ++k) {
+        if (wave + k * kWaves < kInst)
+          *(__attribute__((address_space(3))) u32x4*)(size_t)(base + k * kWaves * 1024 + 16 * lane) = nan4;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the NaN is in LDS before any copy lands
+    }
 #pragma unroll
     for (int k = 0; k < kCopy; ++k) {
       if (wave + k * kWaves < kInst)
@@ -329,7 +342,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   f32x16 sacc[2];
   bf16x8 pk[2][2];
   float m = -1e30f;  // reference max of raw scores (finite start)
-  float l = 0.f;     // running denominator over this lane's keys
+  float l = 0.f;     // running denominator over this lane's keys (fp32 P): for LSE
+  float lb = 0.f;    // the same over the bf16-rounded P the second product uses: for O
 
   // ---- matrix phase of tile j: S_j = K_j Q^T, then O^T += V_{j-1}^T P_{j-1}^T
   // No branches here: for tiles past a wavefront's last row the scores are
@@ -458,16 +472,24 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
       m = m_new;
       l *= alpha;
+      lb *= alpha;
 #pragma unroll
       for (int db = 0; db < G::kDBlocks; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-    // P = exp2(S*c - m*c), rounded to bf16 in pairs into the P^T operand;
-    // the row sum adds the unrounded values in four independent chains.
-    // Masked scores are -inf and c > 0, so their probability is exactly 0.
+    // P = exp2(S*c - m*c), rounded to bf16 in pairs into the P^T operand.
+    // Two row sums: of the fp32 values (four independent chains), which
+    // LSE uses, and of the rounded bf16 pairs (v_dot2 with (1, 1)), which
+    // O is divided by, so that the weights O is built from sum to one
+    // exactly.  (With the lazy max the largest P of a row is not exactly 1,
+    // so dividing the rounded numerator by the unrounded sum would leave a
+    // relative error of up to 2^-9 in O.)  Masked scores are -inf and c > 0,
+    // so their probability is exactly 0.
     const float mc = m * c;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float partb[2] = {0.f, 0.f};
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       u32x4 w[2];
@@ -478,11 +500,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         part[i & 3] += p0;
         part[(i & 3) + 1] += p1;
         const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+        partb[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, partb[(i >> 1) & 1], false);
         w[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(unsigned, pp);
       }
       pk[kb][0] = pin(__builtin_bit_cast(bf16x8, w[0]));
       pk[kb][1] = pin(__builtin_bit_cast(bf16x8, w[1]));
     }
+    lb = pin(lb + (partb[0] + partb[1]));
     l = pin(l + ((part[0] + part[1]) + (part[2] + part[3])));
   };
 
@@ -594,8 +618,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // ---- finalise: one division per row, then O and LSE ----------------------
   const float lt = sum_halves(l);
+  const float ltb = sum_halves(lb);
   if (qrow >= N) return;
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / ltb;
   const long long orow = head + (long long)qrow * D;
 #pragma unroll
   for (int db = 0; db < G::kDBlocks; ++db)
@@ -627,7 +652,7 @@ hipError_t launch_t(const FwdArgs& a) {
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
-                     a.B * a.H, a.N, T, c);
+                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -16,6 +16,9 @@ struct FwdArgs {
   bool causal;
   float scale;
   bool o_bf16;
+  // Debug: fill each LDS ring slot with NaN before a tile is copied into it
+  // (bf16 kernel; set from the FA2_DEBUG_POISON environment variable).
+  bool poison;
   hipStream_t stream;
 };
 

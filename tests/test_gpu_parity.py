@@ -237,3 +237,39 @@ def test_error_status_on_gpu():
     with pytest.raises(fa2.Fa2Error) as e:
         fa2.forward(q, q.clone(), q.clone())
     assert e.value.status == fa2.FA2_ERR_UNSUPPORTED
+
+
+# --- LDS-poison debug mode ------------------------------------------------------
+# With FA2_DEBUG_POISON set, the bf16 kernel fills every LDS ring slot with
+# NaN before a K/V tile is copied into it.  If a wave read a slot before its
+# copy landed, or a copy overwrote a slot still being read, NaN (or another
+# tile's values) would reach O.  When the copy/barrier protocol holds, the
+# poison is always overwritten first, so the result is bit-identical to the
+# ordinary run.
+
+POISON_CASES = [(1, 2, 1000, 64, True), (2, 3, 777, 128, False), (1, 4, 1024, 128, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", POISON_CASES,
+                         ids=[f"{b}x{h}x{n}x{d}-{'causal' if c else 'full'}" for b, h, n, d, c in POISON_CASES])
+def test_lds_poison_small(monkeypatch, B, H, N, d, causal):
+    q, k, v = _inputs(B, H, N, d, "bf16", seed=11, outliers=0.001 if d == 128 else 0.0)
+    scale = 1.0 / math.sqrt(d)
+    o0, l0 = _run(q, k, v, causal, scale)
+    monkeypatch.setenv("FA2_DEBUG_POISON", "1")
+    o1, l1 = _run(q, k, v, causal, scale)
+    monkeypatch.delenv("FA2_DEBUG_POISON")
+    eo, el = ref.attention_ref(_np64(q), _np64(k), _np64(v), scale, causal)
+    _check(o1, l1, eo, el, "bf16", f"poisoned LDS {B}x{H}x{N}x{d} causal={causal}")
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_lds_poison_headline_workload(monkeypatch):
+    w = workloads.get(workloads.HEADLINE)
+    q, k, v = workloads.make_inputs(w, 0, device=DEV)
+    o0, l0 = _run(q, k, v, w.causal, w.scale)
+    monkeypatch.setenv("FA2_DEBUG_POISON", "1")
+    o1, l1 = _run(q, k, v, w.causal, w.scale)
+    monkeypatch.delenv("FA2_DEBUG_POISON")
+    assert torch.isfinite(o1).all().item() and torch.isfinite(l1).all().item()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
