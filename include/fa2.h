@@ -79,8 +79,14 @@ typedef enum fa2_status {
  *
  * Arithmetic: bf16 inputs use bf16 matrix-core products with fp32
  * accumulation, the softmax statistics in fp32, and probabilities rounded
- * to bf16 (nearest-even) before the P*V product.  fp32 inputs keep every
- * step in fp32.
+ * to bf16 (nearest-even) before the P*V product; O is divided by the sum of
+ * those rounded probabilities, the logsumexp uses the sum of the unrounded
+ * ones.  fp32 inputs keep every step in fp32.
+ *
+ * Debug: when the environment variable FA2_DEBUG_POISON is set (and not
+ * "0") at the time of the call, the bf16 kernel fills each shared-memory
+ * tile slot with NaN before copying a K or V tile into it, so a read that
+ * races its copy shows up as NaN in o.  Results are otherwise unchanged.
  *
  * Returns FA2_OK after enqueueing, else a negative fa2_status.
  */

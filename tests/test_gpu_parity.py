@@ -273,3 +273,15 @@ def test_lds_poison_headline_workload(monkeypatch):
     monkeypatch.delenv("FA2_DEBUG_POISON")
     assert torch.isfinite(o1).all().item() and torch.isfinite(l1).all().item()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_headline_whole_heads_every_row():
+    # two whole heads of the headline workload (N = 8192, causal, outliers):
+    # every row against the oracle, not a sample
+    w = workloads.get(workloads.HEADLINE)
+    q, k, v = workloads.make_inputs(w, 0, device=DEV)
+    o, lse = _run(q, k, v, w.causal, w.scale)
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
+        print(f"[parity] {w.name} head ({b},{h}): all {w.N} rows", flush=True)
+        eo, el = ref.attention_head(_np64(q[b, h]), _np64(k[b, h]), _np64(v[b, h]), w.scale, w.causal)
+        _check(o[b, h], lse[b, h], eo, el, w.dtype, f"{w.name} head ({b},{h}) all rows")
