@@ -17,3 +17,9 @@ from .exact_attention import (  # noqa: F401
     tiled_online_attention,
     visible,
 )
+from .attention_grad import (  # noqa: F401
+    attention_grad_head,
+    attention_grad_ref,
+    delta_rows,
+    grad_magnitudes_head,
+)
