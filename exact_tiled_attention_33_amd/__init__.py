@@ -1,4 +1,4 @@
-"""MI355X (gfx950) FlashAttention-2 forward: a thin ctypes binding of libfa2.so.
+"""MI355X (gfx950) FlashAttention-2 forward and backward: a thin ctypes binding of libfa2.so.
 
 The library (``libfa2.so``, built in-tree by ``build_lib``) exports the C ABI
 declared in ``include/fa2.h``.  This module only marshals arguments: every
@@ -7,11 +7,15 @@ fallback -- if the library is missing, every call raises.
 
 Raw entry points (same names and argument order as the C ABI):
     fa2_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, in_dtype, o_dtype) -> int
+    fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale, stream,
+            in_dtype, o_dtype, grad_dtype) -> int
     fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict
     fa2_strerror(status) -> str
     fa2_version() -> int
 Convenience wrapper over torch device tensors:
     forward(q, k, v, causal=False, scale=None, o_dtype=torch.float32) -> (o, lse)
+    backward(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=torch.float32)
+        -> (dq, dk, dv)
 """
 
 from __future__ import annotations
@@ -24,7 +28,7 @@ __all__ = [
     "F32", "BF16",
     "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
     "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
-    "forward", "EXPORTED_SYMBOLS",
+    "fa2_bwd", "forward", "backward", "EXPORTED_SYMBOLS",
 ]
 
 F32 = 0
@@ -36,7 +40,7 @@ FA2_ERR_UNSUPPORTED = -2
 FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_bwd", "fa2_plan", "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -85,6 +89,13 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_bwd.restype = ctypes.c_int
+    lib.fa2_bwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    ]
     lib.fa2_plan.restype = ctypes.c_int
     lib.fa2_plan.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -102,6 +113,13 @@ def fa2_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, in_dtype, o_dtyp
     """Raw C call: pointers and sizes as Python ints; returns the status code."""
     return int(load().fa2_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale),
                               stream, in_dtype, o_dtype))
+
+
+def fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale, stream,
+            in_dtype, o_dtype, grad_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, int(causal),
+                              float(scale), stream, in_dtype, o_dtype, grad_dtype))
 
 
 def fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict:
@@ -169,3 +187,53 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             grad_dtype=None, delta=None, dq=None, dk=None, dv=None, stream=None):
+    """Attention backward on [B, H, N, d] device tensors; returns (dq, dk, dv).
+
+    ``o`` and ``lse`` are what ``forward`` returned for the same q, k, v,
+    causal and scale; ``dout`` is the gradient with respect to o (same dtype
+    as q).  ``grad_dtype`` defaults to float32.  ``delta`` ([B, H, N]
+    float32) is a workspace, allocated when not given.  The kernels are
+    enqueued on ``stream`` (default: torch's current stream) and this
+    returns without synchronising.
+    """
+    import torch
+
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o and dout must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype):
+        raise TypeError("q, k, v and dout must share a dtype")
+    tensors = (q, k, v, o, lse, dout)
+    if not all(t.is_cuda for t in tensors):
+        raise ValueError("all tensors must be device tensors")
+    if not all(t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    outs = []
+    for t in (dq, dk, dv):
+        if t is None:
+            t = torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
+        if t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous [B, H, N, d] tensors of grad_dtype")
+        outs.append(t)
+    dq, dk, dv = outs
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                 lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                 B, H, N, d, causal, scale, handle, _dtype_code(q.dtype), _dtype_code(o.dtype),
+                 _dtype_code(grad_dtype))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_bwd")
+    return dq, dk, dv

@@ -53,7 +53,7 @@ const char* fa2_strerror(int status) {
   switch (status) {
     case FA2_OK: return "success";
     case FA2_ERR_INVALID_ARG: return "invalid argument (null/misaligned/overlapping pointer, bad size, scale or dtype code)";
-    case FA2_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128)";
+    case FA2_ERR_UNSUPPORTED: return "unsupported configuration (forward: head dim 64 or 128; backward: bf16 inputs, head dim 128)";
     case FA2_ERR_NO_DEVICE: return "no HIP device available";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
@@ -136,6 +136,50 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.stream = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = (in_dtype == FA2_BF16) ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+            int causal, float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  if (!is_dtype(o_dtype) || !is_dtype(grad_dtype)) return FA2_ERR_INVALID_ARG;
+  const int st = check_sizes(B, H, N, d, in_dtype);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return FA2_ERR_INVALID_ARG;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t in_bytes = elems * (in_dtype == FA2_BF16 ? 2 : 4);
+  const size_t o_bytes = elems * (o_dtype == FA2_BF16 ? 2 : 4);
+  const size_t g_bytes = elems * (grad_dtype == FA2_BF16 ? 2 : 4);
+  const size_t row_bytes = (size_t)B * H * N * sizeof(float);
+  const void* ins[6] = {q, k, v, dout, o, lse};
+  const size_t in_sz[6] = {in_bytes, in_bytes, in_bytes, in_bytes, o_bytes, row_bytes};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t out_sz[4] = {g_bytes, g_bytes, g_bytes, row_bytes};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA2_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA2_ERR_INVALID_ARG;
+  }
+  if (in_dtype != FA2_BF16 || d != 128) return FA2_ERR_UNSUPPORTED;
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+
+  fa2::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.o_bf16 = (o_dtype == FA2_BF16);
+  a.grad_bf16 = (grad_dtype == FA2_BF16);
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return fa2::launch_bwd_bf16(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -32,6 +32,39 @@ constexpr int kF32Waves = 4;
 constexpr int kF32BlockRows = kF32Waves * 32;    // 128
 constexpr int kF32BlockCols = 32;
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N, d;
+  bool causal;
+  float scale;
+  bool o_bf16;
+  bool grad_bf16;
+  hipStream_t stream;
+};
+
+// Backward tile geometry (bf16 inputs): the dQ kernel gives each of its
+// kBwdQWaves wavefronts 32 query rows and streams 64-key tiles; the dK/dV
+// kernel gives each wavefront of a group 32 keys (kBwdKVKeys per
+// workgroup) and streams 32-query blocks, the two groups taking alternate
+// blocks.
+constexpr int kBwdQWaves = 8;
+constexpr int kBwdQRows = kBwdQWaves * 32;  // 256
+constexpr int kBwdQCols = 64;
+constexpr int kBwdKVKeys = 128;
+constexpr int kBwdKVRows = 32;
+
+// Enqueue the backward kernels (D, dK/dV, dQ) for bf16 inputs.
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+
 // Enqueue the forward kernel for bf16 (resp. fp32) inputs.  Arguments are
 // already validated; returns the launch status.
 hipError_t launch_fwd_bf16(const FwdArgs& a);

@@ -1,5 +1,6 @@
 /*
- * fa2.h -- C ABI of an MI355X (gfx950) FlashAttention-2 forward pass.
+ * fa2.h -- C ABI of an MI355X (gfx950) FlashAttention-2 forward pass and its
+ * backward pass.
  *
  * The operation (exact attention, computed tile by tile with an online
  * softmax, never writing the N x N score matrix to device memory):
@@ -24,14 +25,15 @@
  * causal mode are the parameters of a forward call).
  *
  * Conventions shared by every entry point:
- *   - Tensors are dense, row-major, contiguous: q, k, v, o are [B, H, N, d]
- *     (d fastest), lse is [B, H, N].  Query and key lengths are both N.
+ *   - Tensors are dense, row-major, contiguous: q, k, v, o (and dout, dq,
+ *     dk, dv) are [B, H, N, d] (d fastest); lse (and delta) are [B, H, N].
+ *     Query and key lengths are both N.
  *   - All data pointers are DEVICE pointers on the current HIP device.
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises; it enqueues its kernels on `stream` and returns.  The
  *     caller observes completion through the stream.
- *   - o and lse are fully overwritten (every row, including ragged tails);
- *     q, k and v are only read.  Outputs must not alias inputs.
+ *   - Outputs are fully overwritten (every row, including ragged tails);
+ *     inputs are only read.  Outputs must not alias inputs.
  *   - Arguments are validated before any HIP call; on error nothing is
  *     launched and a negative fa2_status is returned.  No output is printed
  *     and no exception crosses the ABI.
@@ -93,6 +95,58 @@ typedef enum fa2_status {
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int B, int H, int N, int d, int causal, float scale,
             void* stream, int in_dtype, int o_dtype);
+
+/*
+ * fa2_bwd -- attention backward: dQ, dK and dV from the forward's O and LSE.
+ *
+ * The gradient of a scalar loss through the operation of fa2_fwd, given its
+ * gradient dO with respect to O (chain rule through P = softmax of the
+ * scaled, masked scores):
+ *
+ *   P_ij  = exp(S_ij - LSE_i) for visible (i, j), else 0
+ *   D_i   = sum_c dO_ic O_ic                (written to `delta`)
+ *   dV_j  = sum_i P_ij dO_i
+ *   dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *
+ * Sources: the pages define the forward pass only.  The backward pass is
+ * named as part of the training runs behind the headline numbers (Saraf,
+ * "FlashAttention 2: Three Places the Chip Was Still Waiting", section 2.5)
+ * and as something a benchmark must say whether it times (Mishra,
+ * "FlashAttention-2 and -3: From Algebra to GPU Scheduling", the
+ * benchmarking checklist); P is recomputed from q, k and LSE instead of
+ * stored (Mishra, the note that a fast kernel may redo arithmetic to avoid
+ * moving data).  D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.
+ *
+ *   q, k, v, dout  device pointers, [B, H, N, d] in `in_dtype`, 16-byte aligned.
+ *   o              device pointer, [B, H, N, d] in `o_dtype`, 16-byte aligned:
+ *                  the output fa2_fwd returned for the same q, k, v.
+ *   lse            device pointer, [B, H, N] float32: the LSE fa2_fwd returned.
+ *   delta          device pointer, [B, H, N] float32, caller-owned workspace;
+ *                  overwritten with D.
+ *   dq, dk, dv     device pointers, [B, H, N, d] in `grad_dtype`, 16-byte
+ *                  aligned; fully overwritten.
+ *   B, H, N, d, causal, scale, stream: as for fa2_fwd (same values as the
+ *                  forward call).
+ *   in_dtype       FA2_BF16 (q, k, v and dout); FA2_F32: FA2_ERR_UNSUPPORTED.
+ *   o_dtype        FA2_F32 or FA2_BF16 (the dtype o was written in).
+ *   grad_dtype     FA2_F32 or FA2_BF16 for dq, dk, dv (bf16: rounded to
+ *                  nearest-even from the fp32 result).
+ *   d              128 (others: FA2_ERR_UNSUPPORTED).
+ *
+ * Arithmetic: bf16 matrix-core products with fp32 accumulation; P and dS
+ * are rounded to bf16 (nearest-even) before the products that consume them
+ * (dV, and dQ / dK); D and the softmax terms are fp32.
+ *
+ * Outputs must not alias inputs or each other; delta must not alias any of
+ * them.  Three kernels are enqueued on `stream` (D, then dK/dV, then dQ).
+ * Returns FA2_OK after enqueueing, else a negative fa2_status.
+ */
+int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+            const float* lse, float* delta, void* dq, void* dk, void* dv,
+            int B, int H, int N, int d, int causal, float scale,
+            void* stream, int in_dtype, int o_dtype, int grad_dtype);
 
 /*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,

@@ -174,3 +174,49 @@ def test_plan_rejects_what_fwd_rejects():
         fa2.fa2_plan(1, 1, 8, 80, 0, fa2.BF16)
     with pytest.raises(fa2.Fa2Error):
         fa2.fa2_plan(1, 1, 8, 64, 3, fa2.BF16)
+
+
+# --- fa2_bwd argument validation (no compute) --------------------------------
+
+BQ, BK, BV, BO, BG, BL, BD, DQ, DK, DV = (0x10000000 * (i + 1) for i in range(10))
+BGOOD = dict(q=BQ, k=BK, v=BV, o=BO, dout=BG, lse=BL, delta=BD, dq=DQ, dk=DK, dv=DV, B=1, H=2,
+             N=64, d=128, causal=1, scale=0.088, stream=0, in_dtype=fa2.BF16, o_dtype=fa2.F32,
+             grad_dtype=fa2.F32)
+
+
+def _bcall(**over):
+    a = dict(BGOOD, **over)
+    return fa2.fa2_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["delta"], a["dq"],
+                       a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"],
+                       a["stream"], a["in_dtype"], a["o_dtype"], a["grad_dtype"])
+
+
+@pytest.mark.parametrize("over, status", [
+    *[(dict(**{name: 0}), fa2.FA2_ERR_INVALID_ARG)
+      for name in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv")],
+    (dict(B=0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(N=-3), fa2.FA2_ERR_INVALID_ARG),
+    (dict(causal=-1), fa2.FA2_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa2.FA2_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(o_dtype=9), fa2.FA2_ERR_INVALID_ARG),
+    (dict(grad_dtype=2), fa2.FA2_ERR_INVALID_ARG),
+    (dict(in_dtype=5), fa2.FA2_ERR_INVALID_ARG),
+    (dict(dq=DQ + 8), fa2.FA2_ERR_INVALID_ARG),     # misaligned output
+    (dict(delta=BD + 2), fa2.FA2_ERR_INVALID_ARG),  # misaligned workspace
+    (dict(dk=BQ + 256), fa2.FA2_ERR_INVALID_ARG),   # output overlaps q
+    (dict(dv=DK + 64), fa2.FA2_ERR_INVALID_ARG),    # outputs overlap each other
+    (dict(delta=BL + 4), fa2.FA2_ERR_INVALID_ARG),  # workspace overlaps lse
+    (dict(delta=DV + 16), fa2.FA2_ERR_INVALID_ARG),  # workspace overlaps an output
+    (dict(d=64), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(d=96), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa2.F32), fa2.FA2_ERR_UNSUPPORTED),
+])
+def test_bwd_validation_rejects_before_any_hip_call(over, status):
+    assert _bcall(**over) == status
+
+
+@pytest.mark.skipif(_gpu_present(), reason="valid fake pointers would launch on a real GPU")
+def test_bwd_no_device_status_on_cpu_only_host():
+    assert _bcall() == fa2.FA2_ERR_NO_DEVICE
+    assert _bcall(grad_dtype=fa2.BF16, o_dtype=fa2.BF16, causal=0) == fa2.FA2_ERR_NO_DEVICE

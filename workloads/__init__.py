@@ -31,7 +31,8 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "HEADLINE", "make_inputs", "credited_flops", "get"]
+__all__ = ["Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_grad_output", "credited_flops",
+           "credited_bwd_flops", "get"]
 
 
 @dataclass(frozen=True)
@@ -101,6 +102,24 @@ def make_inputs(w: Workload, seed: int, device="cpu"):
         k = torch.where(mk, k * w.outlier_mult, k)
     dt = w.torch_dtype
     return (q.to(dt).to(device), k.to(dt).to(device), v.to(dt).to(device))
+
+
+def make_grad_output(w: Workload, seed: int, device="cpu"):
+    """Draw the upstream gradient dO for workload ``w``: float32 N(0, 1) of
+    shape [B, H, N, d] from a CPU generator seeded with ``seed`` (use a seed
+    distinct from the one the inputs were drawn with), cast to the workload
+    dtype."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.randn(w.shape, generator=g, dtype=torch.float32).to(w.torch_dtype).to(device)
+
+
+def credited_bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Credited attention-backward work: the four N x N x d products
+    (S, dP, dV, and one of dQ / dK) plus the fifth, 10*B*H*N^2*d in all,
+    halved when causal."""
+    f = 10.0 * B * H * N * N * d
+    return f / 2.0 if causal else f
 
 
 def credited_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
