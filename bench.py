@@ -17,6 +17,12 @@ rocprofv3 counters (from the committed summary, if it matches the current
 kernel source), and the fp64 CPU oracle timed on a bounded sample of the
 same workload on the host cores.
 
+With --pass bwd a step is one fa2_bwd call (the D, dK/dV and dQ kernels) on
+the same workload, with dO drawn from the seeded generator and O and LSE
+from one fa2_fwd call made before timing; throughput is credited backward
+work (10*B*H*N^2*d, halved when causal) and the CPU baseline times the fp64
+gradient oracle.
+
 Extra modes used to produce committed profile summaries:
     --calibrate-copy      time a plain 1 GiB device copy (counter calibration)
     --summarize-pmc DIR   summarise rocprofv3 --pmc CSV output found under DIR
@@ -39,10 +45,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPs/s and % of MI355X bf16 MFMA peak, d=128 N=8k causal"
+METRIC_BWD = "attention bwd TFLOPs/s and % of MI355X bf16 MFMA peak, d=128 N=8k causal"
 # Dense bf16 matrix-core peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+BWD_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_bwd_bf16.hip",
+               "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
+               "exact_tiled_attention_33_amd/csrc/fa2_launch.h"]
 KERNEL_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_fwd_bf16.hip",
                   "exact_tiled_attention_33_amd/csrc/fa2_fwd_f32.hip",
                   "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
@@ -50,9 +60,9 @@ KERNEL_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_fwd_bf16.hip",
 CALIB_BYTES = 1 << 30
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -207,6 +217,134 @@ def run_bench(args) -> dict:
     return result
 
 
+def cpu_baseline_bwd(w, q, k, v, g, budget_s: float = 12.0):
+    """Time the fp64 gradient oracle on whole heads until the budget is used
+    (at least one head)."""
+    import torch
+
+    import oracle.attention_grad as gref
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    done, t_total = 0, 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            arrs = [t[b, h].to("cpu", torch.float64).numpy() for t in (q, k, v, g)]
+            t0 = time.perf_counter()
+            gref.attention_grad_head(*arrs, w.scale, w.causal)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    flops = workloads.credited_bwd_flops(1, done, w.N, w.d, w.causal)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.H} (batch, head) pairs of {w.name}, whole heads "
+                  f"(N={w.N}, d={w.d}, causal={w.causal}), fp64 numpy gradient oracle, {t_total:.1f} s",
+        "seconds": t_total,
+    }
+
+
+def run_bench_bwd(args) -> dict:
+    import torch
+
+    import exact_tiled_attention_33_amd as fa2
+    import workloads
+
+    w = workloads.get(args.workload)
+    if w.dtype != "bf16" or w.d != 128:
+        raise SystemExit(f"bench.py --pass bwd: the backward pass covers bf16, d=128 workloads ({w.name} is not)")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    q, k, v = workloads.make_inputs(w, seed=args.seed, device=dev)
+    g = workloads.make_grad_output(w, seed=args.seed + 7919, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        o, lse = fa2.forward(q, k, v, causal=w.causal, scale=w.scale, stream=stream)
+    delta = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
+                 delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N, w.d,
+                 int(w.causal), w.scale, stream.cuda_stream, fa2.BF16, fa2.F32, fa2.F32)
+    torch.cuda.synchronize()
+
+    def step():
+        st = fa2.fa2_bwd(*call_args)
+        if st != fa2.FA2_OK:
+            raise fa2.Fa2Error(st, "fa2_bwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(per_call_ms) / len(per_call_ms)
+    flops = workloads.credited_bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    # executed: dK/dV recomputes S and dP (4 products), dQ does S, dP, dQ (3)
+    executed = 14.0 * w.B * w.H * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC_BWD,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+            "scale": w.scale, "in_dtype": w.dtype, "o_dtype": "fp32", "grad_dtype": "fp32",
+            "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
+            "dropout": 0.0, "backward": True, "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "scope": "one fa2_bwd call (D, dK/dV and dQ kernels), HIP events on its stream",
+            "call_ms_avg": round(avg_ms, 4),
+            "algorithmic_flops_per_call": flops,
+            "executed_flops_per_call": executed,
+        },
+        "timing": {"wall_s": round(wall, 4), "per_call_ms_min": round(min(per_call_ms), 4),
+                   "per_call_ms_max": round(max(per_call_ms), 4)},
+        "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                "cus": props.multi_processor_count},
+        "kernel_source_sha256_16": kernel_source_hash(BWD_SOURCES),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, g, budget_s=args.cpu_budget)
+    return result
+
+
 def calibrate_copy(args) -> None:
     """A plain device-to-device copy of CALIB_BYTES, repeated: its counter
     readings calibrate FETCH_SIZE / WRITE_SIZE against known bytes."""
@@ -249,6 +387,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--o-dtype", choices=["fp32", "bf16"], default="fp32")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="fwd (default): the forward pass; bwd: the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -271,7 +411,7 @@ def main() -> int:
 
     if args.workload is None:
         args.workload = workloads.HEADLINE
-    result = run_bench(args)
+    result = run_bench_bwd(args) if args.which == "bwd" else run_bench(args)
     print(json.dumps(result))
     return 0
 
