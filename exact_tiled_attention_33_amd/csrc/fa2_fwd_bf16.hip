@@ -150,27 +150,29 @@ __device__ __forceinline__ void sched_reads_ahead() {
   }
 }
 
-// Raw buffer descriptor as four scalar registers, for the LDS copy below.
-__device__ __forceinline__ i32x4 raw_rsrc(const void* base, int bytes) {
-  const unsigned long long b = reinterpret_cast<unsigned long long>(base);
-  i32x4 r = {__builtin_amdgcn_readfirstlane((int)(b & 0xffffffffu)),
-             __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xffffu)),
-             __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
-  return r;
-}
-
-// Copy 16 bytes per lane from global memory (buffer rsrc, byte offset
-// voff; zeros past the end) straight into LDS: lane i's bytes land at LDS
-// byte offset lds_offset + 16*i (lds_offset is wave-uniform).  Written as inline assembly so that the compiler does not
-// treat every later LDS read as dependent on the copy (it would wait for all
-// outstanding copies); completion is tracked explicitly with wait_vmem and
-// published with a workgroup barrier.  Clobbers m0, which nothing else in
-// these kernels uses.
+// Copy 16 bytes per lane from global memory (wave-uniform 64-bit base in
+// scalar registers plus a per-lane byte offset; no range check, callers
+// clamp) straight into LDS: lane i's bytes land at LDS byte offset
+// lds_offset + 16*i (lds_offset is wave-uniform).  global_load_lds lands
+// from HBM markedly sooner than the buffer-descriptor form of the same copy
+// (measured ~2,500 against ~3,900 cycles).  Written as inline assembly so
+// that the compiler does not treat every later LDS read as dependent on the
+// copy (it would wait for all outstanding copies); completion is tracked
+// explicitly with wait_vmem and published with a workgroup barrier.
+// Clobbers m0, which nothing else in these kernels uses.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, int voff, unsigned lds_offset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_offset), "v"(voff), "s"(rsrc) : "memory", "m0");
+__device__ __forceinline__ void copy16_to_lds(unsigned long long base, int voff, unsigned lds_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_offset), "v"(voff), "s"(base) : "memory", "m0");
+}
+
+// A wave-uniform 64-bit address in scalar registers.
+__device__ __forceinline__ unsigned long long uniform_addr(const void* p) {
+  const unsigned long long b = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(b & 0xffffffffu));
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  return ((unsigned long long)hi << 32) | lo;
 }
 #pragma clang diagnostic pop
 
@@ -204,13 +206,13 @@ __device__ __forceinline__ T pin(T x) {
 }
 
 // Lazy max correction: the reference max m of a row is only moved (and the
-// banked l and O corrected) when a tile's row max exceeds it by more than
-// this many powers of two, so the unnormalised probabilities stay in
-// [0, 2^32], far inside fp32 range even summed over a million keys.  Any
-// reference value gives the same softmax (the shift cancels between
-// numerator and denominator); Saraf section 2.2: the correction is what
-// keeps the answer exact.
-constexpr float kRescaleThreshold = 32.0f;
+// banked l and O corrected) when the probabilities a tile gives against the
+// current m sum to more than this in one half-row (32 keys), so every
+// unnormalised probability stays in [0, 2^31], far inside fp32 range even
+// summed over a million keys.  Any reference value gives the same softmax
+// (the shift cancels between numerator and denominator); Saraf section 2.2:
+// the correction is what keeps the answer exact.
+constexpr float kTileSumLimit = 2147483648.0f;  // 2^31
 
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
@@ -299,7 +301,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
     constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
     const int key0 = j * kBc;
-    const i32x4 r = raw_rsrc(src + (long long)key0 * D, min(kBc, N - key0) * G::kRowBytes);
+    const int rows = min(kBc, N - key0);
+    const unsigned long long gsrc = uniform_addr(src + (long long)key0 * D);
     const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
     if (poison) {
       // Debug: NaN over the 1 KiB blocks this wave's copies are about to
@@ -314,10 +317,17 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the NaN is in LDS before any copy lands
     }
+    // The last tile of a ragged sequence: rows past N are fetched from row
+    // N-1 instead (global loads have no range check); those keys are masked
+    // in the vector phase, so their K and V values never reach the output.
+    const bool ragged = rows < kBc;
 #pragma unroll
     for (int k = 0; k < kCopy; ++k) {
-      if (wave + k * kWaves < kInst)
-        copy16_to_lds(r, K_TILE ? voff_k[k] : voff_v[k], base + k * kWaves * 1024);
+      if (wave + k * kWaves < kInst) {
+        int vo = K_TILE ? voff_k[k] : voff_v[k];
+        if (ragged) vo = min(vo / G::kRowBytes, rows - 1) * G::kRowBytes + vo % G::kRowBytes;
+        copy16_to_lds(gsrc, vo, base + k * kWaves * 1024);
+      }
     }
   };
   // copy instructions this wave issues per K (V) tile
@@ -341,7 +351,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   f32x16 sacc[2];
   bf16x8 pk[2][2];
-  float m = -1e30f;  // reference max of raw scores (finite start)
+  // Reference max of raw scores.  It is subtracted inside the score MFMA:
+  // each chain starts from the accumulator negm = -m, so the vector phase
+  // sees S - m and a probability is one multiply and one exp2.  m is set by
+  // the first tile (0 until then).
+  float m = 0.f;
+  f32x16 negm;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
   float l = 0.f;     // running denominator over this lane's keys (fp32 P): for LSE
   float lb = 0.f;    // the same over the bf16-rounded P the second product uses: for O
 
@@ -418,7 +435,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const bf16x8 a = op[n % kAhead];
       if (n + kAhead < kNS + kNP) op[n % kAhead] = read_op(n + kAhead);
       if (n < kNS) {
-        sacc[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n >> 1], n < 2 ? f32x16{} : sacc[n & 1], 0, 0, 0);
+        sacc[n & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[n >> 1], n < 2 ? negm : sacc[n & 1], 0, 0, 0);
       } else {
         const int m = n - kNS, db = m % G::kDBlocks, ks = m / G::kDBlocks;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
@@ -435,7 +452,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- vector phase of tile j: mask, row max, correction, P = exp2(...) ----
+  // ---- vector phase of tile j: mask, P = exp2(...), row sums, correction ---
+  // The scores arrive as S - m.  P = exp2((S - m)*c) is computed against the
+  // current reference first; the tile's half-row sums then show whether m
+  // must move (some sum above kTileSumLimit, or not finite), and only then
+  // (or on the first tile, which sets m) is the row max formed, m moved, the
+  // banked l and O^T corrected and P recomputed.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto vector_phase = [&](int j) __attribute__((always_inline)) {
     if (j >= n_full) {
       // element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*half + (i%4);
@@ -452,62 +475,72 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     sacc[0] = pin(sacc[0]);
     sacc[1] = pin(sacc[1]);
-    // Row max in four independent chains (chain r takes the elements
-    // e = 16*kb + i with e % 4 == r), then both halves of the row.
-    auto el = [&](int e) __attribute__((always_inline)) { return sacc[e >> 4][e & 15]; };
-    float mx[4];
+    // P = exp2((S - m)*c - sh*c), rounded to bf16 in pairs into the P^T
+    // operand.  Two row sums: of the fp32 values (independent chains), which
+    // LSE uses, and of the rounded bf16 pairs (v_dot2 with (1, 1)), which O
+    // is divided by, so that the weights O is built from sum to one exactly.
+    // (With the lazy max the largest P of a row is not exactly 1, so
+    // dividing the rounded numerator by the unrounded sum would leave a
+    // relative error of up to 2^-9 in O.)  Masked scores are -inf and c > 0,
+    // so their probability is exactly 0.
+    u32x4 w[2][2];
+    float t, tb;
+    // shift_c: subtract shc (= shift * c) in an FMA, or (common case) none
+    auto probs = [&](auto shift_c, float shc) __attribute__((always_inline)) {
+      constexpr bool kShift = decltype(shift_c)::value;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      float partb[2] = {0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mx[r] = fmaxf(el(r), el(r + 4));
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 8; e < 32; e += 8)
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(kShift ? fmaf(sacc[kb][i], c, -shc) : sacc[kb][i] * c);
+          const float p1 = __builtin_amdgcn_exp2f(kShift ? fmaf(sacc[kb][i + 1], c, -shc) : sacc[kb][i + 1] * c);
+          part[i & 3] += p0;
+          part[(i & 3) + 1] += p1;
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          partb[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, partb[(i >> 1) & 1], false);
+          w[kb][i >> 3][(i & 7) >> 1] = __builtin_bit_cast(unsigned, pp);
+        }
+      t = (part[0] + part[1]) + (part[2] + part[3]);
+      tb = partb[0] + partb[1];
+    };
+    probs(std::false_type{}, 0.f);
+    const bool first = (j == 0);
+    if (first || __builtin_amdgcn_ballot_w64(!(t <= kTileSumLimit))) {
+      // Row max of S - m in four independent chains (chain r takes the
+      // elements e = 16*kb + i with e % 4 == r), then both halves of the row.
+      auto el = [&](int e) __attribute__((always_inline)) { return sacc[e >> 4][e & 15]; };
+      float mx[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx[r] = fmaxf(fmaxf(mx[r], el(e + r)), el(e + r + 4));
-    const float mt = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-    // Move the reference max only when some row's tile max exceeds it by
-    // more than the threshold; then correct the banked terms.  The first
-    // tile always moves it (m starts at -1e30) unless c is vanishingly
-    // small, in which case every probability is 1 and m never matters.
-    if (__builtin_amdgcn_ballot_w64((mt - m) * c > kRescaleThreshold)) {
-      const float m_new = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-      m = m_new;
+      for (int r = 0; r < 4; ++r) mx[r] = fmaxf(el(r), el(r + 4));
+#pragma unroll
+      for (int e = 8; e < 32; e += 8)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(fmaxf(mx[r], el(e + r)), el(e + r + 4));
+      const float mt = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+      // The first tile sets m to its row max (every row sees at least one
+      // key there); later tiles move it up only.
+      const float sh = first ? mt : fmaxf(mt, 0.f);
+      const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-sh * c);
+      m += sh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m;
       l *= alpha;
       lb *= alpha;
 #pragma unroll
       for (int db = 0; db < G::kDBlocks; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      probs(std::true_type{}, sh * c);
     }
-    // P = exp2(S*c - m*c), rounded to bf16 in pairs into the P^T operand.
-    // Two row sums: of the fp32 values (four independent chains), which
-    // LSE uses, and of the rounded bf16 pairs (v_dot2 with (1, 1)), which
-    // O is divided by, so that the weights O is built from sum to one
-    // exactly.  (With the lazy max the largest P of a row is not exactly 1,
-    // so dividing the rounded numerator by the unrounded sum would leave a
-    // relative error of up to 2^-9 in O.)  Masked scores are -inf and c > 0,
-    // so their probability is exactly 0.
-    const float mc = m * c;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-    float partb[2] = {0.f, 0.f};
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      u32x4 w[2];
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][i + 1], c, -mc));
-        part[i & 3] += p0;
-        part[(i & 3) + 1] += p1;
-        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-        partb[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, partb[(i >> 1) & 1], false);
-        w[i >> 3][(i & 7) >> 1] = __builtin_bit_cast(unsigned, pp);
-      }
-      pk[kb][0] = pin(__builtin_bit_cast(bf16x8, w[0]));
-      pk[kb][1] = pin(__builtin_bit_cast(bf16x8, w[1]));
+      pk[kb][0] = pin(__builtin_bit_cast(bf16x8, w[kb][0]));
+      pk[kb][1] = pin(__builtin_bit_cast(bf16x8, w[kb][1]));
     }
-    lb = pin(lb + (partb[0] + partb[1]));
-    l = pin(l + ((part[0] + part[1]) + (part[2] + part[3])));
+    lb = pin(lb + tb);
+    l = pin(l + t);
   };
 
   using True_ = std::true_type;
