@@ -7,6 +7,7 @@ import this package.  The library never does.
 from .exact_attention import (  # noqa: F401
     attention_head,
     attention_ref,
+    attention_ref_gqa,
     attention_rows,
     finalize,
     merge_stats,
@@ -15,11 +16,13 @@ from .exact_attention import (  # noqa: F401
     scores,
     softmax_stats,
     tiled_online_attention,
+    kv_head_of,
     visible,
 )
 from .attention_grad import (  # noqa: F401
     attention_grad_head,
     attention_grad_ref,
+    attention_grad_ref_gqa,
     delta_rows,
     grad_magnitudes_head,
 )

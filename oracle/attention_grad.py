@@ -48,6 +48,7 @@ __all__ = [
     "grad_k",
     "attention_grad_head",
     "attention_grad_ref",
+    "attention_grad_ref_gqa",
     "grad_magnitudes_head",
     "delta_rows",
 ]
@@ -143,3 +144,26 @@ def grad_magnitudes_head(q, k, v, dout, scale: float, causal: bool):
     ads = p * (adp + row)
     return (abs(float(scale)) * (ads @ np.abs(k)), abs(float(scale)) * (ads.T @ np.abs(q)),
             p.T @ np.abs(dout))
+
+
+def attention_grad_ref_gqa(q, k, v, dout, scale: float, causal: bool):
+    """(dQ, dK, dV) with grouped key/value heads: q and dout [B, H, N, d], k
+    and v [B, H_kv, N, d].  A key/value head feeds every query head of its
+    group, so its gradient is the sum of the per-query-head gradients
+    (the adjoint of using one tensor several times)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    if H % Hkv:
+        raise ValueError(f"{H} query heads cannot share {Hkv} key/value heads evenly")
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = fwd.kv_head_of(h, H, Hkv)
+            gq, gk, gv = attention_grad_head(q[b, h], k[b, g], v[b, g], dout[b, h], scale, causal)
+            dq[b, h] = gq
+            dk[b, g] += gk
+            dv[b, g] += gv
+    return dq, dk, dv

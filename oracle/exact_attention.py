@@ -59,6 +59,8 @@ __all__ = [
     "partial_stats",
     "merge_stats",
     "tiled_online_attention",
+    "kv_head_of",
+    "attention_ref_gqa",
 ]
 
 
@@ -261,3 +263,36 @@ def tiled_online_attention(q, k, v, scale: float, causal: bool, block_rows: int 
             normalisations += 1
         lse[ids] = m + np.log(l)
     return o, lse, normalisations
+
+
+# --- grouped key/value heads (GQA / MQA) ------------------------------------
+
+def kv_head_of(h: int, n_heads: int, n_kv_heads: int) -> int:
+    """The key/value head query head ``h`` reads when ``n_heads`` query heads
+    share ``n_kv_heads`` key/value heads in equal, consecutive groups."""
+    return h // (n_heads // n_kv_heads)
+
+
+def attention_ref_gqa(q, k, v, scale: float, causal: bool, row_block: int = 1024):
+    """Exact attention with grouped key/value heads: q [B, H, N, d], k and v
+    [B, H_kv, N, d] with H a multiple of H_kv; query head h attends with key
+    and value head ``kv_head_of(h, H, H_kv)``.  Returns (O [B, H, N, d],
+    LSE [B, H, N]) in fp64.
+
+    papermap "FlashAttention-2" explainer, Chapter 03 ("The Downstream
+    Story") and Chapter 05 ("The variant family"): GQA-aware kernels are
+    among the variants built on the same partitioning; the grouping itself
+    is the plain reading of the name.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, n, _ = q.shape
+    Hkv = k.shape[1]
+    if H % Hkv:
+        raise ValueError(f"{H} query heads cannot share {Hkv} key/value heads evenly")
+    o = np.empty(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, g], v[b, g], scale, causal, row_block=row_block)
+    return o, lse

@@ -185,7 +185,48 @@ def pin_magnitudes_bound_gradients():
             assert np.all(np.abs(gr) <= mg * (1 + 1e-12) + 1e-300), f"|d{name}| exceeds its magnitude"
 
 
+def pin_gqa_grad_finite_differences():
+    """Grouped key/value heads (4 query heads on 2, and on 1): gradients with
+    respect to the shared K and V equal central finite differences of the
+    loss summed over all query heads, each evaluated by explicit loops on
+    the key/value head it reads (0, 0, 1, 1 and 0, 0, 0, 0)."""
+    rng = _rng(2025)
+    n, d = 4, 2
+    for hkv, groups in ((2, [0, 0, 1, 1]), (1, [0, 0, 0, 0])):
+        q = rng.normal(size=(1, 4, n, d))
+        k, v = rng.normal(size=(1, hkv, n, d)), rng.normal(size=(1, hkv, n, d))
+        g = rng.normal(size=(1, 4, n, d))
+        for causal in (False, True):
+            def loss(kk, vv, qq=q):
+                return math.fsum(_loss_loops(qq[0, h].tolist(), kk[0, groups[h]].tolist(),
+                                             vv[0, groups[h]].tolist(), g[0, h].tolist(), 0.7, causal)
+                                 for h in range(4))
+            h_ = 1e-6
+            fk, fv = np.zeros_like(k), np.zeros_like(v)
+            for idx in np.ndindex(*k.shape):
+                kp, km = k.copy(), k.copy()
+                kp[idx] += h_
+                km[idx] -= h_
+                fk[idx] = (loss(kp, v) - loss(km, v)) / (2 * h_)
+                vp, vm = v.copy(), v.copy()
+                vp[idx] += h_
+                vm[idx] -= h_
+                fv[idx] = (loss(k, vp) - loss(k, vm)) / (2 * h_)
+            fq = np.zeros_like(q)
+            for idx in np.ndindex(*q.shape):
+                qp, qm = q.copy(), q.copy()
+                qp[idx] += h_
+                qm[idx] -= h_
+                fq[idx] = (loss(k, v, qp) - loss(k, v, qm)) / (2 * h_)
+            dq, dk, dv = gref.attention_grad_ref_gqa(q, k, v, g, 0.7, causal)
+            tag = f"H_kv={hkv} causal={causal}"
+            _close(dq, fq, 2e-8, "GQA FD dQ " + tag)
+            _close(dk, fk, 2e-8, "GQA FD dK " + tag)
+            _close(dv, fv, 2e-8, "GQA FD dV " + tag)
+
+
 GRAD_PINS = [
+    pin_gqa_grad_finite_differences,
     pin_grad_finite_differences,
     pin_grad_single_key,
     pin_grad_zero_scale,

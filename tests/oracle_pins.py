@@ -299,7 +299,32 @@ def pin_batch_heads():
             _close(lse[b, h], el, 1e-12, f"batch/head ({b},{h}) LSE")
 
 
+def pin_gqa_head_groups():
+    """Grouped key/value heads: with 6 query heads on 3 key/value heads the
+    query heads read key/value heads 0, 0, 1, 1, 2, 2; on 1 they all read 0;
+    on 6 the result is ordinary multi-head attention.  Each query head is
+    checked against the one-head oracle on the key/value head it must use."""
+    rng = _rng(21)
+    n, d = 13, 4
+    q = rng.normal(size=(1, 6, n, d))
+    for hkv, expect in ((3, [0, 0, 1, 1, 2, 2]), (1, [0] * 6), (6, list(range(6)))):
+        k, v = rng.normal(size=(1, hkv, n, d)), rng.normal(size=(1, hkv, n, d))
+        for causal in (False, True):
+            o, lse = ref.attention_ref_gqa(q, k, v, 0.6, causal)
+            for h, g in enumerate(expect):
+                eo, el = ref.attention_head(q[0, h], k[0, g], v[0, g], 0.6, causal)
+                _close(o[0, h], eo, 1e-14, f"GQA H_kv={hkv} head {h} O causal={causal}")
+                _close(lse[0, h], el, 1e-14, f"GQA H_kv={hkv} head {h} LSE causal={causal}")
+    try:
+        ref.attention_ref_gqa(q, rng.normal(size=(1, 4, n, d)), rng.normal(size=(1, 4, n, d)), 0.6, False)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("6 query heads on 4 key/value heads must be rejected")
+
+
 PINS = [
+    pin_gqa_head_groups,
     pin_brute_force,
     pin_hand_cases,
     pin_probability_rows,

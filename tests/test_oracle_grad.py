@@ -37,6 +37,23 @@ def test_matches_torch_float64_autograd(causal):
 
 _orig = {name: getattr(gref, name) for name in ("grad_v", "grad_p", "grad_scores", "grad_q", "grad_k")}
 
+
+def _gqa_last_head_wins(q, k, v, dout, scale, causal):
+    """Planted mistake: a shared key/value head keeps only its last query
+    head's gradient instead of the sum."""
+    import oracle.exact_attention as fwd
+
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    dq, dk, dv = np.empty_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = fwd.kv_head_of(h, H, Hkv)
+            dq[b, h], dk[b, g], dv[b, g] = gref.attention_grad_head(q[b, h], k[b, g], v[b, g], dout[b, h], scale, causal)
+    return dq, dk, dv
+
+
 MUTANTS = {
     "grad_v_untransposed_p": ("grad_v", lambda p, dout: p @ dout if p.shape[0] == dout.shape[0] else p.T @ dout + 1),
     "grad_v_sign": ("grad_v", lambda p, dout: -(p.T @ dout)),
@@ -50,6 +67,7 @@ MUTANTS = {
     "grad_q_transposed_ds": ("grad_q", lambda ds, k, scale: float(scale) * (ds.T @ k)),
     "grad_k_untransposed_ds": ("grad_k", lambda ds, q, scale: float(scale) * (ds @ q)),
     "grad_k_sign": ("grad_k", lambda ds, q, scale: -float(scale) * (ds.T @ q)),
+    "gqa_last_head_wins": ("attention_grad_ref_gqa", _gqa_last_head_wins),
 }
 
 

@@ -69,6 +69,8 @@ MUTANTS = {
     "finalize_lse_sign": ("finalize", lambda m, l, num: (num / l[:, None], m - np.log(l))),
     "finalize_unnormalised": ("finalize", lambda m, l, num: (num, m + np.log(l))),
     "finalize_log2": ("finalize", lambda m, l, num: (num / l[:, None], m + np.log2(l))),
+    "gqa_heads_interleaved": ("kv_head_of", lambda h, n_heads, n_kv: h % n_kv),
+    "gqa_heads_reversed": ("kv_head_of", lambda h, n_heads, n_kv: n_kv - 1 - h // (n_heads // n_kv)),
 }
 
 
