@@ -9,10 +9,12 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, in_dtype, o_dtype) -> int
     fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale, stream,
             in_dtype, o_dtype, grad_dtype) -> int
+    fa2_fwd_gqa / fa2_bwd_gqa: the same with H_kv after H (grouped key/value heads)
     fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict
     fa2_strerror(status) -> str
     fa2_version() -> int
-Convenience wrapper over torch device tensors:
+Convenience wrappers over torch device tensors (k and v may have fewer heads
+than q: grouped key/value heads):
     forward(q, k, v, causal=False, scale=None, o_dtype=torch.float32) -> (o, lse)
     backward(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=torch.float32)
         -> (dq, dk, dv)
@@ -28,7 +30,7 @@ __all__ = [
     "F32", "BF16",
     "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
     "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
-    "fa2_bwd", "forward", "backward", "EXPORTED_SYMBOLS",
+    "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "forward", "backward", "EXPORTED_SYMBOLS",
 ]
 
 F32 = 0
@@ -40,7 +42,8 @@ FA2_ERR_UNSUPPORTED = -2
 FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_bwd", "fa2_plan", "fa2_strerror", "fa2_version")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_bwd", "fa2_bwd_gqa", "fa2_plan", "fa2_strerror",
+                    "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -96,6 +99,19 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_fwd_gqa.restype = ctypes.c_int
+    lib.fa2_fwd_gqa.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+    ]
+    lib.fa2_bwd_gqa.restype = ctypes.c_int
+    lib.fa2_bwd_gqa.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    ]
     lib.fa2_plan.restype = ctypes.c_int
     lib.fa2_plan.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -120,6 +136,19 @@ def fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale,
     """Raw C call: pointers and sizes as Python ints; returns the status code."""
     return int(load().fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, int(causal),
                               float(scale), stream, in_dtype, o_dtype, grad_dtype))
+
+
+def fa2_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, in_dtype, o_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, int(causal), float(scale),
+                                  stream, in_dtype, o_dtype))
+
+
+def fa2_bwd_gqa(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, causal, scale, stream,
+                in_dtype, o_dtype, grad_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_bwd_gqa(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d,
+                                  int(causal), float(scale), stream, in_dtype, o_dtype, grad_dtype))
 
 
 def fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict:
@@ -153,14 +182,17 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
             out=None, lse=None, stream=None):
     """Attention forward on [B, H, N, d] device tensors; returns (o, lse).
 
-    ``o_dtype`` defaults to float32.  ``out``/``lse`` may be given to reuse
+    k and v may be [B, H_kv, N, d] with H_kv dividing H (grouped key/value
+    heads, fa2_fwd_gqa).  ``o_dtype`` defaults to float32.  ``out``/``lse`` may be given to reuse
     buffers.  The kernels are enqueued on ``stream`` (default: torch's
     current stream) and this returns without synchronising.
     """
     import torch
 
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q, k, v must share one [B, H, N, d] shape, got {q.shape}, {k.shape}, {v.shape}")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
+    if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:] or q.shape[1] % k.shape[1]:
+        raise ValueError(f"k, v heads must divide q's and the other dims match, got {q.shape}, {k.shape}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -182,8 +214,9 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                 B, H, N, d, causal, scale, handle, _dtype_code(q.dtype), _dtype_code(o_dtype))
+    st = fa2_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, k.shape[1], N, d, causal, scale, handle, _dtype_code(q.dtype),
+                     _dtype_code(o_dtype))
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse
@@ -195,15 +228,18 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
 
     ``o`` and ``lse`` are what ``forward`` returned for the same q, k, v,
     causal and scale; ``dout`` is the gradient with respect to o (same dtype
-    as q).  ``grad_dtype`` defaults to float32.  ``delta`` ([B, H, N]
+    as q).  k and v may have fewer heads than q (grouped key/value heads);
+    dk and dv then have k's shape.  ``grad_dtype`` defaults to float32.  ``delta`` ([B, H, N]
     float32) is a workspace, allocated when not given.  The kernels are
     enqueued on ``stream`` (default: torch's current stream) and this
     returns without synchronising.
     """
     import torch
 
-    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
-        raise ValueError("q, k, v, o and dout must share one [B, H, N, d] shape")
+    if q.dim() != 4 or any(t.shape != q.shape for t in (o, dout)) or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q, o, dout must be [B, H, N, d] and k, v [B, H_kv, N, d]")
+    if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:] or q.shape[1] % k.shape[1]:
+        raise ValueError(f"k, v heads must divide q's and the other dims match, got {q.shape}, {k.shape}")
     if not (q.dtype == k.dtype == v.dtype == dout.dtype):
         raise TypeError("q, k, v and dout must share a dtype")
     tensors = (q, k, v, o, lse, dout)
@@ -220,20 +256,20 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     outs = []
-    for t in (dq, dk, dv):
+    for t, shape in ((dq, q.shape), (dk, k.shape), (dv, k.shape)):
         if t is None:
-            t = torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
-        if t.shape != q.shape or t.dtype != grad_dtype or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous [B, H, N, d] tensors of grad_dtype")
+            t = torch.empty(shape, dtype=grad_dtype, device=q.device)
+        if t.shape != shape or t.dtype != grad_dtype or not t.is_contiguous():
+            raise ValueError("dq (q's shape), dk, dv (k's shape) must be contiguous tensors of grad_dtype")
         outs.append(t)
     dq, dk, dv = outs
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                 lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                 B, H, N, d, causal, scale, handle, _dtype_code(q.dtype), _dtype_code(o.dtype),
-                 _dtype_code(grad_dtype))
+    st = fa2_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                     lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                     B, H, k.shape[1], N, d, causal, scale, handle, _dtype_code(q.dtype),
+                     _dtype_code(o.dtype), _dtype_code(grad_dtype))
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_bwd")
     return dq, dk, dv

@@ -103,7 +103,14 @@ int fa2_plan(int B, int H, int N, int d, int causal, int in_dtype, int block_row
 
 int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
             int d, int causal, float scale, void* stream, int in_dtype, int o_dtype) {
+  return fa2_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream, in_dtype, o_dtype);
+}
+
+int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int H_kv, int N, int d, int causal, float scale, void* stream, int in_dtype,
+                int o_dtype) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+  if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
   if (!is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
   const int st = check_sizes(B, H, N, d, in_dtype);
@@ -112,12 +119,15 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA2_ERR_INVALID_ARG;
   const size_t elems = (size_t)B * H * N * d;
-  const size_t in_bytes = elems * (in_dtype == FA2_BF16 ? 2 : 4);
+  const size_t esz = in_dtype == FA2_BF16 ? 2 : 4;
+  const size_t q_bytes = elems * esz;
+  const size_t kv_bytes = (size_t)B * H_kv * N * d * esz;
   const size_t o_bytes = elems * (o_dtype == FA2_BF16 ? 2 : 4);
   const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
   const void* ins[3] = {q, k, v};
-  for (const void* in : ins) {
-    if (overlaps(o, o_bytes, in, in_bytes) || overlaps(lse, lse_bytes, in, in_bytes))
+  const size_t in_sz[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, o_bytes, ins[i], in_sz[i]) || overlaps(lse, lse_bytes, ins[i], in_sz[i]))
       return FA2_ERR_INVALID_ARG;
   }
   if (overlaps(o, o_bytes, lse, lse_bytes)) return FA2_ERR_INVALID_ARG;
@@ -128,6 +138,7 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   fa2::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.H = H; a.N = N; a.d = d;
+  a.Hkv = H_kv;
   a.causal = causal != 0;
   a.scale = scale;
   a.o_bf16 = (o_dtype == FA2_BF16);
@@ -141,7 +152,16 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d,
             int causal, float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype) {
+  return fa2_bwd_gqa(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H, N, d, causal, scale, stream,
+                     in_dtype, o_dtype, grad_dtype);
+}
+
+int fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int H_kv,
+                int N, int d, int causal, float scale, void* stream, int in_dtype, int o_dtype,
+                int grad_dtype) {
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
+  if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
   if (!is_dtype(o_dtype) || !is_dtype(grad_dtype)) return FA2_ERR_INVALID_ARG;
   const int st = check_sizes(B, H, N, d, in_dtype);
@@ -151,14 +171,15 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
     return FA2_ERR_INVALID_ARG;
   const size_t elems = (size_t)B * H * N * d;
-  const size_t in_bytes = elems * (in_dtype == FA2_BF16 ? 2 : 4);
+  const size_t kv_elems = (size_t)B * H_kv * N * d;
+  const size_t esz = in_dtype == FA2_BF16 ? 2 : 4;
+  const size_t gsz = grad_dtype == FA2_BF16 ? 2 : 4;
   const size_t o_bytes = elems * (o_dtype == FA2_BF16 ? 2 : 4);
-  const size_t g_bytes = elems * (grad_dtype == FA2_BF16 ? 2 : 4);
   const size_t row_bytes = (size_t)B * H * N * sizeof(float);
   const void* ins[6] = {q, k, v, dout, o, lse};
-  const size_t in_sz[6] = {in_bytes, in_bytes, in_bytes, in_bytes, o_bytes, row_bytes};
+  const size_t in_sz[6] = {elems * esz, kv_elems * esz, kv_elems * esz, elems * esz, o_bytes, row_bytes};
   const void* outs[4] = {dq, dk, dv, delta};
-  const size_t out_sz[4] = {g_bytes, g_bytes, g_bytes, row_bytes};
+  const size_t out_sz[4] = {elems * gsz, kv_elems * gsz, kv_elems * gsz, row_bytes};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA2_ERR_INVALID_ARG;
@@ -174,6 +195,7 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.delta = delta;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.N = N; a.d = d;
+  a.Hkv = H_kv;
   a.causal = causal != 0;
   a.scale = scale;
   a.o_bf16 = (o_dtype == FA2_BF16);

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV.  Grid: blockIdx.x = key tile * BH + bh (key tiles in ascending
+// dK and dV.  Grid: blockIdx.x = key tile * B*Hkv + key/value head (key tiles in ascending
 // order: under a causal mask the first tiles see the most queries).
 constexpr int kKVWaves = 8;
 constexpr int kKVKeys = kBwdKVKeys;                    // 128 = 4 waves x 32 keys
@@ -213,7 +213,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kKVWaves * 64, kKVWaves * 
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                      const __bf16* __restrict__ dout, const float* __restrict__ lse,
                      const float* __restrict__ delta, void* __restrict__ dk, void* __restrict__ dv,
-                     int BH, int N, float c, float scale) {
+                     int BHkv, int N, float c, float scale, int group) {
   __shared__ __attribute__((aligned(1024))) char smem[kKVLds];
   const char* const lds_k = smem;
   const char* const lds_v = smem + kKVTileBytes;
@@ -225,10 +225,14 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int gw = wave & 3;    // keys 32*gw .. +31 of the tile
   const int l32 = lane & 31, half = lane >> 5;
 
-  const int bh = blockIdx.x % BH;
-  const int kt = blockIdx.x / BH;
+  // Grid: key/value head bkv, key tile kt.  With grouped heads the `group`
+  // query heads bkv*group .. bkv*group + group-1 all read this head, and its
+  // dK, dV sum over them: the query blocks of every one of them are
+  // streamed through the same accumulators.
+  const int bkv = blockIdx.x % BHkv;
+  const int kt = blockIdx.x / BHkv;
   const int k0 = kt * kKVKeys;
-  const long long head = (long long)bh * N * kD;
+  const long long head = (long long)bkv * N * kD;  // K, V, dK, dV
   const int kw0 = k0 + 32 * gw;  // first key of this wave
   const int key = kw0 + l32;     // this lane's key
 
@@ -247,16 +251,22 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   // ---- query blocks ----
+  // The work is the list of (query head, block) pairs, query head major;
+  // step s of wave group grp takes item 2s + grp.
   const int nqb = (N + kQB - 1) / kQB;
   const int b_first = CAUSAL ? k0 / kQB : 0;
-  const int n_steps = (nqb - b_first + 1) / 2;
-  // group-local copy of block b into ring slot `slot`: Q and dO 8
+  const int nb = nqb - b_first;  // blocks per query head
+  const int n_items = group * nb;
+  const int n_steps = (n_items + 1) / 2;
+  // group-local copy of item it into ring slot `slot`: Q and dO 8
   // instructions each (2 per wave), then the LSE and D rows.
-  auto copy_block = [&](int b, int slot) __attribute__((always_inline)) {
-    const int q0 = b * kQB;
+  auto copy_block = [&](int it, int slot) __attribute__((always_inline)) {
+    const int hq = bkv * group + it / nb;  // query head
+    const int q0 = (b_first + it % nb) * kQB;
+    const long long qhead = (long long)hq * N * kD;
     const int rows = max(0, min(kQB, N - q0));
-    const i32x4 rq = raw_rsrc(q + head + (long long)q0 * kD, rows * kRowBytes);
-    const i32x4 rg = raw_rsrc(dout + head + (long long)q0 * kD, rows * kRowBytes);
+    const i32x4 rq = raw_rsrc(q + qhead + (long long)q0 * kD, rows * kRowBytes);
+    const i32x4 rg = raw_rsrc(dout + qhead + (long long)q0 * kD, rows * kRowBytes);
     const unsigned base =
         __builtin_amdgcn_readfirstlane(lds_offset_of(lds_ring)) + (unsigned)((grp * 2 + slot) * kSlotBytes);
 #pragma unroll
@@ -266,7 +276,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       copy16_to_lds(rg, copy_voff(lane, i), base + kQBBytes + 1024 * i);
     }
     if (gw < 2) {
-      const float* src = (gw == 0 ? lse : delta) + (long long)bh * N + q0;
+      const float* src = (gw == 0 ? lse : delta) + (long long)hq * N + q0;
       copy4_to_lds(raw_rsrc(src, rows * 4), 4 * lane, base + 2 * kQBBytes + 256 * gw);
     }
   };
@@ -366,19 +376,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
   };
 
-  // Prologue: K, V and each group's first block in LDS.
-  if (b_first + grp < nqb) copy_block(b_first + grp, 0);
+  // Prologue: K, V and each group's first item in LDS.
+  if (grp < n_items) copy_block(grp, 0);
   wait_vmem(0);
   __syncthreads();
-  // Step s: this group's block b_first + 2s + grp from ring slot s % 2,
-  // while the block of step s+1 is copied into the other slot (last read in
-  // step s-1, which every wave finished before the barrier that ended it).
+  // Step s: this group's item 2s + grp from ring slot s % 2, while the item
+  // of step s+1 is copied into the other slot (last read in step s-1, which
+  // every wave finished before the barrier that ended it).
   auto step = [&](int s, auto slot_c) __attribute__((always_inline)) {
     constexpr int kSl = decltype(slot_c)::value;
-    const int b = b_first + 2 * s + grp;
-    if (b + 2 < nqb) copy_block(b + 2, kSl ^ 1);
+    const int it = 2 * s + grp;
+    if (it + 2 < n_items) copy_block(it + 2, kSl ^ 1);
+    const int b = b_first + it % nb;
     // a block lying wholly above this wave's keys (causal) contributes 0
-    if (b < nqb && !(CAUSAL && b * kQB + kQB <= kw0)) compute(b, slot_c);
+    if (it < n_items && !(CAUSAL && b * kQB + kQB <= kw0)) compute(b, slot_c);
     wait_vmem(0);
     __syncthreads();
   };
@@ -443,7 +454,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kQWaves * 64, kQWaves * 64
 void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                    const __bf16* __restrict__ dout, const float* __restrict__ lse,
                    const float* __restrict__ delta, void* __restrict__ dq, int BH, int N, int T, float c,
-                   float scale) {
+                   float scale, int group) {
   __shared__ __attribute__((aligned(1024))) char smem[kQRing * kQStage];
 
   const int lane = threadIdx.x & 63;
@@ -454,6 +465,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
   const int tr = blockIdx.x / BH;
   const int t = CAUSAL ? (T - 1 - tr) : tr;
   const long long head = (long long)bh * N * kD;
+  // grouped key/value heads: `group` consecutive query heads share one
+  const long long kv_head = (long long)(bh / group) * N * kD;
   const int q0 = t * kQRows;
   const int qw = q0 + 32 * wave;
   const int qrow = qw + l32;
@@ -489,8 +502,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
   auto copy_tile = [&](int j) __attribute__((always_inline)) {
     const int key0 = j * kQCols;
     const int rows = min(kQCols, N - key0);
-    const i32x4 rk = raw_rsrc(k + head + (long long)key0 * kD, rows * kRowBytes);
-    const i32x4 rv = raw_rsrc(v + head + (long long)key0 * kD, rows * kRowBytes);
+    const i32x4 rk = raw_rsrc(k + kv_head + (long long)key0 * kD, rows * kRowBytes);
+    const i32x4 rv = raw_rsrc(v + kv_head + (long long)key0 * kD, rows * kRowBytes);
     const unsigned base = lds0 + (unsigned)((j % kQRing) * kQStage);
 #pragma unroll
     for (int m = 0; m < kQCols / 4 / kQWaves; ++m) {
@@ -592,18 +605,20 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
 template <bool CAUSAL, bool GRAD_BF16>
 hipError_t launch_bwd_t(const BwdArgs& a, float c) {
   const int BH = a.B * a.H;
-  const long long kv_grid = (long long)((a.N + kKVKeys - 1) / kKVKeys) * BH;
+  const int BHkv = a.B * a.Hkv;
+  const int group = a.H / a.Hkv;
+  const long long kv_grid = (long long)((a.N + kKVKeys - 1) / kKVKeys) * BHkv;
   const int T = (a.N + kQRows - 1) / kQRows;
   const long long q_grid = (long long)T * BH;
   if (kv_grid > 0x7fffffffLL || q_grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, GRAD_BF16>), dim3((unsigned)kv_grid), dim3(kKVWaves * 64), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                     a.delta, a.dk, a.dv, BH, a.N, c, a.scale);
+                     a.delta, a.dk, a.dv, BHkv, a.N, c, a.scale, group);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL, GRAD_BF16>), dim3((unsigned)q_grid), dim3(kQWaves * 64), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                     a.delta, a.dq, BH, a.N, T, c, a.scale);
+                     a.delta, a.dq, BH, a.N, T, c, a.scale, group);
   return hipGetLastError();
 }
 

@@ -218,7 +218,7 @@ template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
-                     int BH, int N, int T, float c, int poison) {
+                     int BH, int N, int T, float c, int poison, int group) {
   using G = Geo<D>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
@@ -241,8 +241,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int t = CAUSAL ? (T - 1 - tr) : tr;
 
   const long long head = (long long)bh * N * D;
-  const __bf16* kh = k + head;
-  const __bf16* vh = v + head;
+  // grouped key/value heads: `group` consecutive query heads share one
+  const long long kv_head = (long long)(bh / group) * N * D;
+  const __bf16* kh = k + kv_head;
+  const __bf16* vh = v + kv_head;
 
   // Rows: the two wavefronts of a SIMD take adjacent 32-row slices, so the
   // causal work of the two groups stays balanced.
@@ -685,7 +687,7 @@ hipError_t launch_t(const FwdArgs& a) {
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
-                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0);
+                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     const float* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
-                    int BH, int N, int T, float c, float scale) {
+                    int BH, int N, int T, float c, float scale, int group) {
   using G = GeoF<D>;
   __shared__ __attribute__((aligned(16))) float smem[G::kLdsFloats];
 
@@ -74,9 +74,11 @@ void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   const int tr = blockIdx.x / BH;
   const int t = CAUSAL ? (T - 1 - tr) : tr;
   const long long head = (long long)bh * N * D;
+  // grouped key/value heads: `group` consecutive query heads share one
+  const long long kv_head = (long long)(bh / group) * N * D;
   const float* qh = q + head;
-  const float* kh = k + head;
-  const float* vh = v + head;
+  const float* kh = k + kv_head;
+  const float* vh = v + kv_head;
 
   const int q0 = t * kBr;
   const int qw = q0 + wave * kRows;
@@ -224,7 +226,7 @@ hipError_t launch_t(const FwdArgs& a) {
   const float c = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.o, a.lse,
-                     a.B * a.H, a.N, T, c, a.scale);
+                     a.B * a.H, a.N, T, c, a.scale, a.H / a.Hkv);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, N, d;
+  int Hkv;  // key/value heads (H for ordinary multi-head attention)
   bool causal;
   float scale;
   bool o_bf16;
@@ -44,6 +45,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   int B, H, N, d;
+  int Hkv;  // key/value heads (H for ordinary multi-head attention)
   bool causal;
   float scale;
   bool o_bf16;

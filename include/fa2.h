@@ -97,6 +97,30 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             void* stream, int in_dtype, int o_dtype);
 
 /*
+ * fa2_fwd_gqa -- fa2_fwd with grouped key/value heads (GQA; MQA when
+ * H_kv = 1).
+ *
+ * The H query heads of a sequence share H_kv key/value heads in equal,
+ * consecutive groups: query head h attends with key/value head
+ * h / (H / H_kv).  Everything else is fa2_fwd; fa2_fwd(...) is
+ * fa2_fwd_gqa(...) with H_kv = H.
+ *
+ * Source: papermap "FlashAttention-2" explainer, Chapter 03 ("The
+ * Downstream Story") and Chapter 05 ("The variant family"): GQA-aware
+ * kernels are named among the variants built on FlashAttention-2's
+ * partitioning; the grouping is the plain reading of the name.
+ *
+ *   q, o      [B, H, N, d]; lse [B, H, N].
+ *   k, v      [B, H_kv, N, d].
+ *   H_kv      >= 1 and dividing H (else FA2_ERR_INVALID_ARG).
+ *
+ * Returns FA2_OK after enqueueing, else a negative fa2_status.
+ */
+int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int H_kv, int N, int d, int causal, float scale,
+                void* stream, int in_dtype, int o_dtype);
+
+/*
  * fa2_bwd -- attention backward: dQ, dK and dV from the forward's O and LSE.
  *
  * The gradient of a scalar loss through the operation of fa2_fwd, given its
@@ -147,6 +171,21 @@ int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const vo
             const float* lse, float* delta, void* dq, void* dk, void* dv,
             int B, int H, int N, int d, int causal, float scale,
             void* stream, int in_dtype, int o_dtype, int grad_dtype);
+
+/*
+ * fa2_bwd_gqa -- fa2_bwd with grouped key/value heads (see fa2_fwd_gqa).
+ *
+ * q, o, dout, dq: [B, H, N, d]; lse, delta: [B, H, N]; k, v, dk, dv:
+ * [B, H_kv, N, d].  A key/value head is used by every query head of its
+ * group, so its dK and dV are the sums over that group's query heads
+ * (computed in one pass per key/value head, no atomics).  fa2_bwd(...) is
+ * fa2_bwd_gqa(...) with H_kv = H.  Returns FA2_OK after enqueueing, else a
+ * negative fa2_status.
+ */
+int fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, float* delta, void* dq, void* dk, void* dv,
+                int B, int H, int H_kv, int N, int d, int causal, float scale,
+                void* stream, int in_dtype, int o_dtype, int grad_dtype);
 
 /*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,

@@ -220,3 +220,41 @@ def test_bwd_validation_rejects_before_any_hip_call(over, status):
 def test_bwd_no_device_status_on_cpu_only_host():
     assert _bcall() == fa2.FA2_ERR_NO_DEVICE
     assert _bcall(grad_dtype=fa2.BF16, o_dtype=fa2.BF16, causal=0) == fa2.FA2_ERR_NO_DEVICE
+
+
+# --- grouped key/value heads (fa2_fwd_gqa, fa2_bwd_gqa) ----------------------
+
+def _gcall(H=8, H_kv=2, **over):
+    a = dict(GOOD, H=H, **over)
+    return fa2.fa2_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], H_kv, a["N"],
+                           a["d"], a["causal"], a["scale"], a["stream"], a["in_dtype"], a["o_dtype"])
+
+
+def _gbcall(H=8, H_kv=2, **over):
+    a = dict(BGOOD, H=H, **over)
+    return fa2.fa2_bwd_gqa(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["delta"], a["dq"],
+                           a["dk"], a["dv"], a["B"], a["H"], H_kv, a["N"], a["d"], a["causal"],
+                           a["scale"], a["stream"], a["in_dtype"], a["o_dtype"], a["grad_dtype"])
+
+
+@pytest.mark.parametrize("H, H_kv", [(8, 0), (8, -2), (8, 3), (6, 4), (4, 8)])
+def test_gqa_rejects_head_counts_that_do_not_divide(H, H_kv):
+    assert _gcall(H=H, H_kv=H_kv) == fa2.FA2_ERR_INVALID_ARG
+    assert _gbcall(H=H, H_kv=H_kv) == fa2.FA2_ERR_INVALID_ARG
+
+
+def test_gqa_overlap_checks_use_the_key_value_sizes():
+    # q, o: 1 x 8 x 64 x 64 bf16/fp32; k, v: 1 x 2 x 64 x 64 bf16 = 16 KiB each
+    kv_bytes = 1 * 2 * 64 * 64 * 2
+    assert _gcall(o=K + kv_bytes - 16) == fa2.FA2_ERR_INVALID_ARG   # o starts inside k
+    bkv = 1 * 2 * 64 * 128 * 4                                       # dk fp32
+    assert _gbcall(dv=DK + bkv - 16) == fa2.FA2_ERR_INVALID_ARG      # dv starts inside dk
+
+
+@pytest.mark.skipif(_gpu_present(), reason="valid fake pointers would launch on a real GPU")
+def test_gqa_no_device_status_on_cpu_only_host():
+    assert _gcall() == fa2.FA2_ERR_NO_DEVICE
+    assert _gcall(H=8, H_kv=1) == fa2.FA2_ERR_NO_DEVICE
+    assert _gbcall() == fa2.FA2_ERR_NO_DEVICE
+    # o right after the (smaller) key buffer does not overlap it
+    assert _gcall(o=K + 1 * 2 * 64 * 64 * 2) == fa2.FA2_ERR_NO_DEVICE
