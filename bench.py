@@ -17,6 +17,10 @@ rocprofv3 counters (from the committed summary, if it matches the current
 kernel source), and the fp64 CPU oracle timed on a bounded sample of the
 same workload on the host cores.
 
+With --kv-heads K (K dividing H) the key/value tensors have K heads and the
+grouped-head entry points run (fa2_fwd_gqa / fa2_bwd_gqa); the credited work
+is unchanged (it counts query heads).
+
 With --pass bwd a step is one fa2_bwd call (the D, dK/dV and dQ kernels) on
 the same workload, with dO drawn from the seeded generator and O and LSE
 from one fa2_fwd call made before timing; throughput is credited backward
@@ -98,9 +102,10 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     done, t_total = 0, 0.0
     for b, h in heads:
+        g = h * k.shape[1] // w.H  # key/value head of query head h
         qh = q[b, h].to("cpu", torch.float64).numpy()
-        kh = k[b, h].to("cpu", torch.float64).numpy()
-        vh = v[b, h].to("cpu", torch.float64).numpy()
+        kh = k[b, g].to("cpu", torch.float64).numpy()
+        vh = v[b, g].to("cpu", torch.float64).numpy()
         t0 = time.perf_counter()
         ref.attention_head(qh, kh, vh, w.scale, w.causal)
         t_total += time.perf_counter() - t0
@@ -121,6 +126,14 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
     }
 
 
+def kv_heads(args, w) -> int:
+    """Key/value heads of the run: --kv-heads if given (grouped heads), else H."""
+    hkv = args.kv_heads or w.H
+    if hkv < 1 or w.H % hkv:
+        raise SystemExit(f"bench.py: --kv-heads {hkv} must divide H = {w.H}")
+    return hkv
+
+
 def run_bench(args) -> dict:
     import torch
 
@@ -132,6 +145,8 @@ def run_bench(args) -> dict:
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     q, k, v = workloads.make_inputs(w, seed=args.seed, device=dev)
+    hkv = kv_heads(args, w)
+    k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     o_dtype = torch.bfloat16 if args.o_dtype == "bf16" else torch.float32
     o = torch.empty(w.shape, dtype=o_dtype, device=dev)
     lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
@@ -140,11 +155,11 @@ def run_bench(args) -> dict:
     o_code = fa2.BF16 if args.o_dtype == "bf16" else fa2.F32
     handle = stream.cuda_stream
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 w.B, w.H, w.N, w.d, int(w.causal), w.scale, handle, in_code, o_code)
+                 w.B, w.H, hkv, w.N, w.d, int(w.causal), w.scale, handle, in_code, o_code)
     torch.cuda.synchronize()
 
     def step():
-        st = fa2.fa2_fwd(*call_args)
+        st = fa2.fa2_fwd_gqa(*call_args)
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st)
 
@@ -170,7 +185,7 @@ def run_bench(args) -> dict:
     value = flops * args.steps / wall / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = traffic_from_profiles(w.name)
+    traffic = traffic_from_profiles(w.name) if hkv == w.H else None
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
 
     result = {
@@ -188,7 +203,7 @@ def run_bench(args) -> dict:
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-            "scale": w.scale, "in_dtype": w.dtype, "o_dtype": args.o_dtype,
+            "scale": w.scale, "in_dtype": w.dtype, "o_dtype": args.o_dtype, "kv_heads": hkv,
             "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
             "dropout": 0.0, "backward": False, "parallelism": "single GPU",
         },
@@ -233,7 +248,8 @@ def cpu_baseline_bwd(w, q, k, v, g, budget_s: float = 12.0):
     done, t_total = 0, 0.0
     for b in range(w.B):
         for h in range(w.H):
-            arrs = [t[b, h].to("cpu", torch.float64).numpy() for t in (q, k, v, g)]
+            kvh = h * k.shape[1] // w.H  # key/value head of query head h
+            arrs = [t[b, i].to("cpu", torch.float64).numpy() for t, i in ((q, h), (k, kvh), (v, kvh), (g, h))]
             t0 = time.perf_counter()
             gref.attention_grad_head(*arrs, w.scale, w.causal)
             t_total += time.perf_counter() - t0
@@ -267,19 +283,22 @@ def run_bench_bwd(args) -> dict:
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     q, k, v = workloads.make_inputs(w, seed=args.seed, device=dev)
+    hkv = kv_heads(args, w)
+    k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     g = workloads.make_grad_output(w, seed=args.seed + 7919, device=dev)
     stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(stream):
         o, lse = fa2.forward(q, k, v, causal=w.causal, scale=w.scale, stream=stream)
     delta = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty(w.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    dq = torch.empty(w.shape, dtype=torch.float32, device=dev)
+    dk, dv = (torch.empty(k.shape, dtype=torch.float32, device=dev) for _ in range(2))
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
-                 delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N, w.d,
+                 delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, hkv, w.N, w.d,
                  int(w.causal), w.scale, stream.cuda_stream, fa2.BF16, fa2.F32, fa2.F32)
     torch.cuda.synchronize()
 
     def step():
-        st = fa2.fa2_bwd(*call_args)
+        st = fa2.fa2_bwd_gqa(*call_args)
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st, "fa2_bwd")
 
@@ -317,7 +336,7 @@ def run_bench_bwd(args) -> dict:
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-            "scale": w.scale, "in_dtype": w.dtype, "o_dtype": "fp32", "grad_dtype": "fp32",
+            "scale": w.scale, "in_dtype": w.dtype, "o_dtype": "fp32", "grad_dtype": "fp32", "kv_heads": hkv,
             "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
             "dropout": 0.0, "backward": True, "parallelism": "single GPU",
         },
@@ -389,6 +408,8 @@ def main() -> int:
     ap.add_argument("--o-dtype", choices=["fp32", "bf16"], default="fp32")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="fwd (default): the forward pass; bwd: the backward pass")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="key/value heads (grouped heads; default: as many as query heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
