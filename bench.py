@@ -183,10 +183,24 @@ def run_bench(args) -> dict:
 
     flops = workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal)
     value = flops * args.steps / wall / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = traffic_from_profiles(w.name) if hkv == w.H else None
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
+    # Algorithmic bytes per launch: Q, K, V read once, O and LSE written once.
+    esz = 2 if w.dtype == "bf16" else 4
+    alg_bytes = (w.B * w.H * w.N * w.d * esz + 2 * w.B * hkv * w.N * w.d * esz
+                 + w.B * w.H * w.N * w.d * (2 if args.o_dtype == "bf16" else 4) + w.B * w.H * w.N * 4)
+    # The kernel is bound by whichever roof its arithmetic intensity is under.
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm_bound = flops / alg_bytes < ridge
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(alg_bytes / (avg_launch_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(alg_bytes / (avg_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
 
     result = {
         "metric": METRIC,
@@ -209,14 +223,14 @@ def run_bench(args) -> dict:
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": round(peak, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            **roof,
             "traffic": traffic,
             "kernel_ms_avg": round(avg_launch_ms, 4),
             "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "arithmetic_intensity": round(flops / alg_bytes, 1),
+            "ridge_flop_per_byte": round(ridge, 1),
+            "achieved_tflops": round(flops / (avg_launch_ms * 1e-3) / 1e12, 2),
             "executed_flops_per_launch": plan["flops_executed"],
         },
         "timing": {"events_span_ms": round(span_ms, 4), "wall_s": round(wall, 4),
