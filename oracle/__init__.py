@@ -8,6 +8,8 @@ from .exact_attention import (  # noqa: F401
     attention_head,
     attention_ref,
     attention_ref_gqa,
+    attention_ref_window,
+    attention_head_window,
     attention_rows,
     finalize,
     merge_stats,
@@ -18,6 +20,8 @@ from .exact_attention import (  # noqa: F401
     tiled_online_attention,
     kv_head_of,
     visible,
+    visible_window,
+    probabilities_window,
 )
 from .attention_grad import (  # noqa: F401
     attention_grad_head,

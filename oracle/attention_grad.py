@@ -49,6 +49,9 @@ __all__ = [
     "attention_grad_head",
     "attention_grad_ref",
     "attention_grad_ref_gqa",
+    "attention_grad_head_window",
+    "attention_grad_ref_window",
+    "grad_magnitudes_head_window",
     "grad_magnitudes_head",
     "delta_rows",
 ]
@@ -99,11 +102,43 @@ def attention_grad_head(q, k, v, dout, scale: float, causal: bool):
     (``exact_attention.probabilities``).
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
-    p = fwd.probabilities(q, k, scale, causal)
+    return _grads_from_p(fwd.probabilities(q, k, scale, causal), q, k, v, dout, scale)
+
+
+def _grads_from_p(p, q, k, v, dout, scale):
+    """The chain rule from the normalised probabilities P of one head."""
     dv = grad_v(p, dout)
     dp = grad_p(dout, v)
     ds = grad_scores(p, dp)
     return grad_q(ds, k, scale), grad_k(ds, q, scale), dv
+
+
+def attention_grad_head_window(q, k, v, dout, scale: float, window_left: int, window_right: int):
+    """(dQ, dK, dV) of one head under a sliding-window mask
+    (``exact_attention.visible_window``): the same chain rule, with P from
+    ``exact_attention.probabilities_window``."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    return _grads_from_p(fwd.probabilities_window(q, k, scale, window_left, window_right), q, k, v, dout, scale)
+
+
+def attention_grad_ref_window(q, k, v, dout, scale: float, window_left: int, window_right: int):
+    """(dQ, dK, dV) over [B, H, N, d] under a sliding window; k and v may have
+    fewer heads (grouped heads: a shared head's gradient is the group sum)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            g = fwd.kv_head_of(h, H, Hkv)
+            gq, gk, gv = attention_grad_head_window(q[b, h], k[b, g], v[b, g], dout[b, h], scale,
+                                                    window_left, window_right)
+            dq[b, h] = gq
+            dk[b, g] += gk
+            dv[b, g] += gv
+    return dq, dk, dv
 
 
 def attention_grad_ref(q, k, v, dout, scale: float, causal: bool):
@@ -138,7 +173,17 @@ def grad_magnitudes_head(q, k, v, dout, scale: float, causal: bool):
     multiple of u times these magnitudes.
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
-    p = fwd.probabilities(q, k, scale, causal)
+    return _magnitudes_from_p(fwd.probabilities(q, k, scale, causal), q, k, v, dout, scale)
+
+
+def grad_magnitudes_head_window(q, k, v, dout, scale: float, window_left: int, window_right: int):
+    """``grad_magnitudes_head`` under a sliding-window mask."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    return _magnitudes_from_p(fwd.probabilities_window(q, k, scale, window_left, window_right),
+                              q, k, v, dout, scale)
+
+
+def _magnitudes_from_p(p, q, k, v, dout, scale):
     adp = np.abs(grad_p(dout, v))
     row = (np.abs(dout) * (p @ np.abs(v))).sum(axis=1, keepdims=True)
     ads = p * (adp + row)

@@ -61,6 +61,10 @@ __all__ = [
     "tiled_online_attention",
     "kv_head_of",
     "attention_ref_gqa",
+    "visible_window",
+    "attention_head_window",
+    "attention_ref_window",
+    "probabilities_window",
 ]
 
 
@@ -296,3 +300,65 @@ def attention_ref_gqa(q, k, v, scale: float, causal: bool, row_block: int = 1024
             g = kv_head_of(h, H, Hkv)
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, g], v[b, g], scale, causal, row_block=row_block)
     return o, lse
+
+
+# --- sliding-window (local) attention ---------------------------------------
+
+def visible_window(row_ids, key_ids, window_left: int, window_right: int) -> np.ndarray:
+    """Boolean mask [len(row_ids), len(key_ids)]: key j is visible to query i
+    iff i - window_left <= j <= i + window_right, a negative bound meaning
+    no limit on that side.  (-1, 0) is the causal mask, (-1, -1) none.
+
+    papermap "FlashAttention-2" explainer, Chapter 03 ("The Downstream
+    Story") and Chapter 05 ("The variant family") name sliding-window
+    attention among the variants built on FlashAttention-2's partitioning;
+    a band of keys around each query, bounded on either side, is the plain
+    reading of the name.
+    """
+    rows = np.asarray(row_ids)[:, None]
+    cols = np.asarray(key_ids)[None, :]
+    vis = np.ones((rows.shape[0], cols.shape[1]), dtype=bool)
+    if window_left >= 0:
+        vis &= cols >= rows - window_left
+    if window_right >= 0:
+        vis &= cols <= rows + window_right
+    return vis
+
+
+def attention_head_window(q, k, v, scale: float, window_left: int, window_right: int):
+    """Exact attention of one head under a sliding-window mask; every row
+    must see at least one key (true whenever both bounds are >= 0 or
+    unbounded).  Returns (O [N, d], LSE [N]) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    ids = np.arange(q.shape[0])
+    s = scores(q, k, scale)
+    mask = visible_window(ids, np.arange(k.shape[0]), window_left, window_right)
+    m, l, num = softmax_stats(s, mask, v)
+    return finalize(m, l, num)
+
+
+def attention_ref_window(q, k, v, scale: float, window_left: int, window_right: int):
+    """Sliding-window attention over [B, H, N, d] (k, v may have fewer heads:
+    grouped heads as in ``attention_ref_gqa``).  Returns (O, LSE) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    o = np.empty(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            o[b, h], lse[b, h] = attention_head_window(q[b, h], k[b, g], v[b, g], scale, window_left, window_right)
+    return o, lse
+
+
+def probabilities_window(q, k, scale: float, window_left: int, window_right: int) -> np.ndarray:
+    """Normalised attention probabilities of one head under a sliding window."""
+    q, k = _f64(q), _f64(k)
+    ids = np.arange(q.shape[0])
+    s = scores(q, k, scale)
+    mask = visible_window(ids, np.arange(k.shape[0]), window_left, window_right)
+    s_vis = np.where(mask, s, -np.inf)
+    m = s_vis.max(axis=1)
+    p = np.exp(np.where(mask, s - m[:, None], -np.inf))
+    return p / p.sum(axis=1, keepdims=True)

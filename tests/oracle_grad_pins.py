@@ -225,7 +225,45 @@ def pin_gqa_grad_finite_differences():
             _close(dv, fv, 2e-8, "GQA FD dV " + tag)
 
 
+def _loss_loops_window(q, k, v, g, scale, wl, wr):
+    """sum_i g_i . O_i under a sliding window, by explicit loops."""
+    n, d, dv = len(q), len(q[0]), len(v[0])
+    total = []
+    for i in range(n):
+        keys = [j for j in range(len(k)) if (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)]
+        s = {j: scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in keys}
+        den = math.fsum(w.values())
+        for c in range(dv):
+            total.append(g[i][c] * math.fsum(w[j] * v[j][c] for j in keys) / den)
+    return math.fsum(total)
+
+
+def pin_window_grad_finite_differences():
+    """Sliding windows: gradients == central finite differences of the
+    loop-evaluated loss."""
+    rng = _rng(2026)
+    h = 1e-6
+    for trial, (wl, wr) in enumerate(((1, 0), (2, 1), (0, 0), (-1, 1), (1, -1))):
+        n = 5
+        q, k, v, g = (rng.normal(size=(n, 2)) for _ in range(4))
+        ref_grads = gref.attention_grad_head_window(q, k, v, g, 0.9, wl, wr)
+        for which in range(3):
+            base = [q, k, v][which]
+            fd = np.zeros_like(base)
+            for idx in np.ndindex(*base.shape):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                up = _loss_loops_window(*(a.tolist() for a in args), g.tolist(), 0.9, wl, wr)
+                args[which][idx] -= 2 * h
+                dn = _loss_loops_window(*(a.tolist() for a in args), g.tolist(), 0.9, wl, wr)
+                fd[idx] = (up - dn) / (2 * h)
+            _close(ref_grads[which], fd, 2e-8, f"window ({wl},{wr}) FD d{'QKV'[which]}")
+
+
 GRAD_PINS = [
+    pin_window_grad_finite_differences,
     pin_gqa_grad_finite_differences,
     pin_grad_finite_differences,
     pin_grad_single_key,

@@ -323,7 +323,62 @@ def pin_gqa_head_groups():
         raise AssertionError("6 query heads on 4 key/value heads must be rejected")
 
 
+def _brute_force_window(q, k, v, scale, wl, wr):
+    """Sliding-window attention by explicit loops: the keys of row i are
+    those j with i - wl <= j (if wl >= 0) and j <= i + wr (if wr >= 0)."""
+    n, d, dv = len(q), len(q[0]), len(v[0])
+    o = [[0.0] * dv for _ in range(n)]
+    lse = [0.0] * n
+    for i in range(n):
+        keys = [j for j in range(len(k)) if (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)]
+        s = {j: scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in keys}
+        den = math.fsum(w.values())
+        for c in range(dv):
+            o[i][c] = math.fsum(w[j] * v[j][c] for j in keys) / den
+        lse[i] = mx + math.log(den)
+    return np.array(o), np.array(lse)
+
+
+def pin_window_brute_force():
+    """Sliding windows on tiny random heads: oracle == explicit loops."""
+    rng = _rng(31)
+    for trial in range(8):
+        n = int(rng.integers(1, 9))
+        q, k, v = rng.normal(size=(n, 3)), rng.normal(size=(n, 3)), rng.normal(size=(n, 2))
+        for wl, wr in ((0, 0), (1, 0), (2, 3), (-1, 2), (3, -1), (-1, 0), (-1, -1), (0, 2)):
+            eo, el = _brute_force_window(q.tolist(), k.tolist(), v.tolist(), 0.8, wl, wr)
+            o, lse = ref.attention_head_window(q, k, v, 0.8, wl, wr)
+            _close(o, eo, 1e-12, f"window ({wl},{wr}) O trial {trial}")
+            _close(lse, el, 1e-12, f"window ({wl},{wr}) LSE trial {trial}")
+
+
+def pin_window_special_cases():
+    """Window (0, 0): each row sees only its own key, so O_i = v_i and
+    LSE_i = S_ii.  Window (-1, 0) is the causal mask; (-1, -1) and windows
+    of at least N keys on both sides are no mask at all."""
+    rng = _rng(32)
+    n, d = 11, 5
+    q, k, v = rng.normal(size=(n, d)), rng.normal(size=(n, d)), rng.normal(size=(n, 3))
+    o, lse = ref.attention_head_window(q, k, v, 0.6, 0, 0)
+    _close(o, v, 1e-14, "window (0,0) O = V")
+    _close(lse, 0.6 * np.einsum("id,id->i", q, k), 1e-13, "window (0,0) LSE = S_ii")
+    oc, lc = ref.attention_head(q, k, v, 0.6, True)
+    for wl, wr, (eo, el) in ((-1, 0, (oc, lc)), (n, 0, (oc, lc))):
+        o, lse = ref.attention_head_window(q, k, v, 0.6, wl, wr)
+        _close(o, eo, 1e-14, f"window ({wl},{wr}) vs causal O")
+        _close(lse, el, 1e-14, f"window ({wl},{wr}) vs causal LSE")
+    of, lf = ref.attention_head(q, k, v, 0.6, False)
+    for wl, wr in ((-1, -1), (n, n), (-1, n)):
+        o, lse = ref.attention_head_window(q, k, v, 0.6, wl, wr)
+        _close(o, of, 1e-14, f"window ({wl},{wr}) vs full O")
+        _close(lse, lf, 1e-14, f"window ({wl},{wr}) vs full LSE")
+
+
 PINS = [
+    pin_window_brute_force,
+    pin_window_special_cases,
     pin_gqa_head_groups,
     pin_brute_force,
     pin_hand_cases,

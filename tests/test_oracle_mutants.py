@@ -18,6 +18,7 @@ _orig_scores = ref.scores
 _orig_visible = ref.visible
 _orig_stats = ref.softmax_stats
 _orig_finalize = ref.finalize
+_orig_visible_window = ref.visible_window
 
 
 def _stats_no_shift(s, mask, v):
@@ -70,6 +71,10 @@ MUTANTS = {
     "finalize_unnormalised": ("finalize", lambda m, l, num: (num, m + np.log(l))),
     "finalize_log2": ("finalize", lambda m, l, num: (num / l[:, None], m + np.log2(l))),
     "gqa_heads_interleaved": ("kv_head_of", lambda h, n_heads, n_kv: h % n_kv),
+    "window_left_strict": ("visible_window", lambda r, c, wl, wr: (
+        (np.ones((len(r), len(c)), dtype=bool) if wl < 0 else np.asarray(c)[None, :] > np.asarray(r)[:, None] - wl)
+        & (np.ones((len(r), len(c)), dtype=bool) if wr < 0 else np.asarray(c)[None, :] <= np.asarray(r)[:, None] + wr))),
+    "window_sides_swapped": ("visible_window", lambda r, c, wl, wr: _orig_visible_window(r, c, wr, wl)),
     "gqa_heads_reversed": ("kv_head_of", lambda h, n_heads, n_kv: n_kv - 1 - h // (n_heads // n_kv)),
 }
 
