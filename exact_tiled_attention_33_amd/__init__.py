@@ -10,6 +10,7 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale, stream,
             in_dtype, o_dtype, grad_dtype) -> int
     fa2_fwd_gqa / fa2_bwd_gqa: the same with H_kv after H (grouped key/value heads)
+    fa2_fwd_window: fa2_fwd_gqa with (window_left, window_right) instead of causal
     fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict
     fa2_strerror(status) -> str
     fa2_version() -> int
@@ -30,7 +31,8 @@ __all__ = [
     "F32", "BF16",
     "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
     "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
-    "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "forward", "backward", "EXPORTED_SYMBOLS",
+    "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "forward", "backward",
+    "EXPORTED_SYMBOLS",
 ]
 
 F32 = 0
@@ -42,8 +44,8 @@ FA2_ERR_UNSUPPORTED = -2
 FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_bwd", "fa2_bwd_gqa", "fa2_plan", "fa2_strerror",
-                    "fa2_version")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa", "fa2_plan",
+                    "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -105,6 +107,12 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_fwd_window.restype = ctypes.c_int
+    lib.fa2_fwd_window.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+    ]
     lib.fa2_bwd_gqa.restype = ctypes.c_int
     lib.fa2_bwd_gqa.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -144,6 +152,13 @@ def fa2_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, in_dty
                                   stream, in_dtype, o_dtype))
 
 
+def fa2_fwd_window(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, scale, stream,
+                   in_dtype, o_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_fwd_window(q, k, v, o, lse, B, H, H_kv, N, d, int(window_left),
+                                     int(window_right), float(scale), stream, in_dtype, o_dtype))
+
+
 def fa2_bwd_gqa(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, causal, scale, stream,
                 in_dtype, o_dtype, grad_dtype) -> int:
     """Raw C call: pointers and sizes as Python ints; returns the status code."""
@@ -179,11 +194,13 @@ def _dtype_code(dt) -> int:
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=None,
-            out=None, lse=None, stream=None):
+            out=None, lse=None, stream=None, window=None):
     """Attention forward on [B, H, N, d] device tensors; returns (o, lse).
 
     k and v may be [B, H_kv, N, d] with H_kv dividing H (grouped key/value
-    heads, fa2_fwd_gqa).  ``o_dtype`` defaults to float32.  ``out``/``lse`` may be given to reuse
+    heads, fa2_fwd_gqa).  ``window=(left, right)`` selects a sliding-window
+    mask (fa2_fwd_window; -1 = unbounded side) and overrides ``causal``.
+    ``o_dtype`` defaults to float32.  ``out``/``lse`` may be given to reuse
     buffers.  The kernels are enqueued on ``stream`` (default: torch's
     current stream) and this returns without synchronising.
     """
@@ -214,9 +231,10 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = fa2_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, H, k.shape[1], N, d, causal, scale, handle, _dtype_code(q.dtype),
-                     _dtype_code(o_dtype))
+    wl, wr = (-1, 0 if causal else -1) if window is None else window
+    st = fa2_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, k.shape[1], N, d, wl, wr, scale, handle, _dtype_code(q.dtype),
+                        _dtype_code(o_dtype))
     if st != FA2_OK:
         raise Fa2Error(st)
     return out, lse

@@ -109,12 +109,27 @@ int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int H_kv, int N, int d, int causal, float scale, void* stream, int in_dtype,
                 int o_dtype) {
-  if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
-  if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  return fa2_fwd_window(q, k, v, o, lse, B, H, H_kv, N, d, -1, causal ? 0 : -1, scale, stream, in_dtype,
+                        o_dtype);
+}
+
+int fa2_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int H_kv, int N, int d, int window_left, int window_right, float scale, void* stream,
+                   int in_dtype, int o_dtype) {
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1) return FA2_ERR_INVALID_ARG;
+  if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
   if (!is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
   const int st = check_sizes(B, H, N, d, in_dtype);
   if (st != FA2_OK) return st;
+  // a bound of N or more keys is no bound (this also keeps the kernels'
+  // index arithmetic in range)
+  const int wl = window_left >= N ? -1 : window_left;
+  const int wr = window_right >= N ? -1 : window_right;
+  const bool causal = (wl == -1 && wr == 0);
+  // the fp32 kernel implements no mask and the causal mask only
+  if (in_dtype == FA2_F32 && !(wl == -1 && (wr == -1 || wr == 0))) return FA2_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA2_ERR_INVALID_ARG;
@@ -139,7 +154,9 @@ int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.Hkv = H_kv;
-  a.causal = causal != 0;
+  a.causal = causal;
+  a.wl = wl;
+  a.wr = wr;
   a.scale = scale;
   a.o_bf16 = (o_dtype == FA2_BF16);
   const char* dbg = std::getenv("FA2_DEBUG_POISON");

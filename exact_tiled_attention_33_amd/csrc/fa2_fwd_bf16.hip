@@ -214,11 +214,11 @@ __device__ __forceinline__ T pin(T x) {
 // the correction is what keeps the answer exact.
 constexpr float kTileSumLimit = 2147483648.0f;  // 2^31
 
-template <int D, bool CAUSAL, bool OUT_BF16>
+template <int D, bool MASKED, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
-                     int BH, int N, int T, float c, int poison, int group) {
+                     int BH, int N, int T, float c, int poison, int group, int wl, int wr) {
   using G = Geo<D>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
@@ -238,7 +238,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // heaviest (latest rows) first.
   const int bh = blockIdx.x % BH;
   const int tr = blockIdx.x / BH;
-  const int t = CAUSAL ? (T - 1 - tr) : tr;
+  const int t = MASKED ? (T - 1 - tr) : tr;
 
   const long long head = (long long)bh * N * D;
   // grouped key/value heads: `group` consecutive query heads share one
@@ -264,16 +264,33 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (l32 * D + 16 * s + 8 * half) * 2));
   }
 
-  // Key tiles: the workgroup streams n_tiles of them; this wavefront computes
-  // on the first n_w (causal: those starting at or below its last row) and
-  // masks the ones from n_full on (crossing its diagonal, or the ragged end).
+  // Key tiles.  Key j is visible to query i iff i - wl <= j <= i + wr (a
+  // negative bound: no limit on that side; causal is wl < 0, wr = 0).  The
+  // workgroup streams key tiles j_lo .. j_lo + n_tiles - 1, those holding
+  // any key visible to one of its rows; tiles above or below a wavefront's
+  // rows are computed but fully masked.  This wavefront needs no mask on
+  // tiles jf_lo .. jf_hi - 1, whose keys (all below N) every one of its rows
+  // sees.
   const int nk = (N + kBc - 1) / kBc;
-  int n_tiles = nk, n_w = (qw < N) ? nk : 0, n_full = N / kBc;
-  if (CAUSAL) {
-    n_tiles = min(nk, (min(q0 + kBr, N) - 1) / kBc + 1);
-    n_w = (qw < N) ? min(nk, (min(qw + kRows, N) - 1) / kBc + 1) : 0;
-    n_full = min(n_full, (qw + 1) / kBc);
+  int j_lo = 0, n_tiles = nk, jf_lo = 0, jf_hi = N / kBc;
+  if (MASKED) {
+    const int q_last = min(q0 + kBr, N) - 1;
+    const int w_last = min(qw + kRows, N) - 1;
+    if (wl >= 0) {
+      j_lo = max(0, q0 - wl) / kBc;
+      jf_lo = (max(0, w_last - wl) + kBc - 1) / kBc;
+    }
+    int j_hi = nk;
+    if (wr >= 0) {
+      j_hi = min(nk, (q_last + wr) / kBc + 1);
+      jf_hi = min(jf_hi, qw + wr - (kBc - 1) >= 0 ? (qw + wr - (kBc - 1)) / kBc + 1 : 0);
+    }
+    n_tiles = j_hi - j_lo;
   }
+  // This row's visible keys, [key_lo, key_hi]: the mask is two compares per
+  // score (no per-element branching on which bounds exist).
+  const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
+  const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
 
   // Tile copies: instruction i of a tile fills LDS slots [64i, 64i + 64);
   // slot u is (row u / slots-per-row, chunk u % slots-per-row), and the
@@ -302,7 +319,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr bool K_TILE = decltype(is_k)::value;
     constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
     constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
-    const int key0 = j * kBc;
+    const int key0 = (j_lo + j) * kBc;
     const int rows = min(kBc, N - key0);
     const unsigned long long gsrc = uniform_addr(src + (long long)key0 * D);
     const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
@@ -358,6 +375,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // sees S - m and a probability is one multiply and one exp2.  m is set by
   // the first tile (0 until then).
   float m = 0.f;
+  bool m_set = false;  // this row has met a visible key (m is its reference)
   f32x16 negm;
 #pragma unroll
   for (int i = 0; i < 16; ++i) negm[i] = 0.f;
@@ -462,17 +480,16 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // banked l and O^T corrected and P recomputed.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto vector_phase = [&](int j) __attribute__((always_inline)) {
-    if (j >= n_full) {
-      // element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*half + (i%4);
-      // tiles at or past n_w lie wholly above this wave's rows -> all masked
-      const int key0 = j * kBc;
+    const int ja = j_lo + j;  // key tile index
+    if (ja < jf_lo || ja >= jf_hi) {
+      // element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*half + (i%4)
+      const int key0 = ja * kBc;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool vis = (key < N) && (!CAUSAL || key <= qrow);
-          if (!vis) sacc[kb][i] = -INFINITY;
+          sacc[kb][i] = (key >= key_lo) & (key <= key_hi) ? sacc[kb][i] : -INFINITY;
         }
     }
     sacc[0] = pin(sacc[0]);
@@ -508,8 +525,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       tb = partb[0] + partb[1];
     };
     probs(std::false_type{}, 0.f);
-    const bool first = (j == 0);
-    if (first || __builtin_amdgcn_ballot_w64(!(t <= kTileSumLimit))) {
+    if (__builtin_amdgcn_ballot_w64(!m_set || !(t <= kTileSumLimit))) {
       // Row max of S - m in four independent chains (chain r takes the
       // elements e = 16*kb + i with e % 4 == r), then both halves of the row.
       auto el = [&](int e) __attribute__((always_inline)) { return sacc[e >> 4][e & 15]; };
@@ -521,10 +537,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx[r] = fmaxf(fmaxf(mx[r], el(e + r)), el(e + r + 4));
       const float mt = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
-      // The first tile sets m to its row max (every row sees at least one
-      // key there); later tiles move it up only.
-      const float sh = first ? mt : fmaxf(mt, 0.f);
-      const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-sh * c);
+      // A row's first tile with a visible key sets m to that tile's row max
+      // (l and O^T are still 0); later tiles move it up only.
+      const bool has_key = mt > -INFINITY;
+      const float sh = m_set ? fmaxf(mt, 0.f) : (has_key ? mt : 0.f);
+      const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh * c) : 0.f;
+      m_set = m_set || has_key;
       m += sh;
 #pragma unroll
       for (int i = 0; i < 16; ++i) negm[i] = -m;
@@ -676,7 +694,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (half == 0) lse[(long long)bh * N + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16>
+template <int D, bool MASKED, bool OUT_BF16>
 hipError_t launch_t(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)T * a.B * a.H;
@@ -685,15 +703,15 @@ hipError_t launch_t(const FwdArgs& a) {
   // exactly 0 even for scale == 0; any c that small already makes every
   // probability exactly 1 in fp32.
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
-                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv);
+                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a) {
-  if (a.causal) return a.o_bf16 ? launch_t<D, true, true>(a) : launch_t<D, true, false>(a);
+  if (a.wl >= 0 || a.wr >= 0) return a.o_bf16 ? launch_t<D, true, true>(a) : launch_t<D, true, false>(a);
   return a.o_bf16 ? launch_t<D, false, true>(a) : launch_t<D, false, false>(a);
 }
 

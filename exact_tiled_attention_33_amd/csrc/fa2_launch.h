@@ -15,6 +15,9 @@ struct FwdArgs {
   int B, H, N, d;
   int Hkv;  // key/value heads (H for ordinary multi-head attention)
   bool causal;
+  // Sliding window: key j visible to query i iff i - wl <= j <= i + wr; -1 =
+  // no limit on that side (causal: wl = -1, wr = 0; none: both -1).
+  int wl, wr;
   float scale;
   bool o_bf16;
   // Debug: fill each LDS ring slot with NaN before a tile is copied into it

@@ -121,6 +121,32 @@ int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse
                 void* stream, int in_dtype, int o_dtype);
 
 /*
+ * fa2_fwd_window -- fa2_fwd_gqa with a sliding-window (local) mask.
+ *
+ * Key j is visible to query i iff
+ *     i - window_left <= j <= i + window_right,
+ * where a bound of -1 means no limit on that side and a bound of N or more
+ * is the same as no limit.  (-1, 0) is the causal mask and (-1, -1) no
+ * mask: fa2_fwd_gqa(..., causal, ...) is fa2_fwd_window with those bounds.
+ * Every query sees at least its own key, so every row is defined.  Key
+ * tiles wholly outside a query tile's band are never loaded.
+ *
+ * Source: papermap "FlashAttention-2" explainer, Chapter 03 ("The
+ * Downstream Story") and Chapter 05 ("The variant family"): sliding-window
+ * kernels are named among the variants built on FlashAttention-2's
+ * partitioning; a band of keys around each query is the plain reading.
+ *
+ *   window_left, window_right  >= -1 (else FA2_ERR_INVALID_ARG).
+ *   in_dtype FA2_F32 supports only (-1, -1) and (-1, 0) (else
+ *   FA2_ERR_UNSUPPORTED).
+ * All other arguments as fa2_fwd_gqa.  Returns FA2_OK after enqueueing,
+ * else a negative fa2_status.
+ */
+int fa2_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, int window_left, int window_right,
+                   float scale, void* stream, int in_dtype, int o_dtype);
+
+/*
  * fa2_bwd -- attention backward: dQ, dK and dV from the forward's O and LSE.
  *
  * The gradient of a scalar loss through the operation of fa2_fwd, given its

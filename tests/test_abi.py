@@ -258,3 +258,30 @@ def test_gqa_no_device_status_on_cpu_only_host():
     assert _gbcall() == fa2.FA2_ERR_NO_DEVICE
     # o right after the (smaller) key buffer does not overlap it
     assert _gcall(o=K + 1 * 2 * 64 * 64 * 2) == fa2.FA2_ERR_NO_DEVICE
+
+
+# --- sliding-window forward (fa2_fwd_window) ---------------------------------
+
+def _wcall(wl, wr, **over):
+    a = dict(GOOD, **over)
+    return fa2.fa2_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H"], a["N"],
+                              a["d"], wl, wr, a["scale"], a["stream"], a["in_dtype"], a["o_dtype"])
+
+
+@pytest.mark.parametrize("wl, wr", [(-2, 0), (0, -3), (-5, -5)])
+def test_window_rejects_bounds_below_minus_one(wl, wr):
+    assert _wcall(wl, wr) == fa2.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("wl, wr", [(0, 0), (10, 0), (-1, 5), (3, 3)])
+def test_window_fp32_supports_only_no_mask_and_causal(wl, wr):
+    assert _wcall(wl, wr, in_dtype=fa2.F32) == fa2.FA2_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(_gpu_present(), reason="valid fake pointers would launch on a real GPU")
+def test_window_no_device_status_on_cpu_only_host():
+    for wl, wr in ((-1, -1), (-1, 0), (0, 0), (100, 7)):
+        assert _wcall(wl, wr) == fa2.FA2_ERR_NO_DEVICE
+    # bounds of N or more are no bounds: fp32 accepts them as no mask / causal
+    assert _wcall(64, 0, in_dtype=fa2.F32) == fa2.FA2_ERR_NO_DEVICE
+    assert _wcall(1000, 1000, in_dtype=fa2.F32) == fa2.FA2_ERR_NO_DEVICE
