@@ -10,7 +10,8 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, N, d, causal, scale, stream,
             in_dtype, o_dtype, grad_dtype) -> int
     fa2_fwd_gqa / fa2_bwd_gqa: the same with H_kv after H (grouped key/value heads)
-    fa2_fwd_window: fa2_fwd_gqa with (window_left, window_right) instead of causal
+    fa2_fwd_window / fa2_bwd_window: the *_gqa calls with (window_left, window_right)
+        instead of causal (sliding-window mask)
     fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict
     fa2_strerror(status) -> str
     fa2_version() -> int
@@ -31,7 +32,7 @@ __all__ = [
     "F32", "BF16",
     "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
     "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
-    "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "forward", "backward",
+    "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "fa2_bwd_window", "forward", "backward",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -44,8 +45,8 @@ FA2_ERR_UNSUPPORTED = -2
 FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa", "fa2_plan",
-                    "fa2_strerror", "fa2_version")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
+                    "fa2_bwd_window", "fa2_plan", "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -113,6 +114,13 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_bwd_window.restype = ctypes.c_int
+    lib.fa2_bwd_window.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+    ]
     lib.fa2_bwd_gqa.restype = ctypes.c_int
     lib.fa2_bwd_gqa.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -157,6 +165,14 @@ def fa2_fwd_window(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right,
     """Raw C call: pointers and sizes as Python ints; returns the status code."""
     return int(load().fa2_fwd_window(q, k, v, o, lse, B, H, H_kv, N, d, int(window_left),
                                      int(window_right), float(scale), stream, in_dtype, o_dtype))
+
+
+def fa2_bwd_window(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, window_left, window_right,
+                   scale, stream, in_dtype, o_dtype, grad_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_bwd_window(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d,
+                                     int(window_left), int(window_right), float(scale), stream, in_dtype,
+                                     o_dtype, grad_dtype))
 
 
 def fa2_bwd_gqa(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, causal, scale, stream,
@@ -241,13 +257,14 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
-             grad_dtype=None, delta=None, dq=None, dk=None, dv=None, stream=None):
+             grad_dtype=None, delta=None, dq=None, dk=None, dv=None, stream=None, window=None):
     """Attention backward on [B, H, N, d] device tensors; returns (dq, dk, dv).
 
     ``o`` and ``lse`` are what ``forward`` returned for the same q, k, v,
     causal and scale; ``dout`` is the gradient with respect to o (same dtype
     as q).  k and v may have fewer heads than q (grouped key/value heads);
-    dk and dv then have k's shape.  ``grad_dtype`` defaults to float32.  ``delta`` ([B, H, N]
+    dk and dv then have k's shape.  ``window=(left, right)`` as in ``forward``
+    (it must match the forward call).  ``grad_dtype`` defaults to float32.  ``delta`` ([B, H, N]
     float32) is a workspace, allocated when not given.  The kernels are
     enqueued on ``stream`` (default: torch's current stream) and this
     returns without synchronising.
@@ -284,10 +301,11 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = fa2_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                     lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                     B, H, k.shape[1], N, d, causal, scale, handle, _dtype_code(q.dtype),
-                     _dtype_code(o.dtype), _dtype_code(grad_dtype))
+    wl, wr = (-1, 0 if causal else -1) if window is None else window
+    st = fa2_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                        lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        B, H, k.shape[1], N, d, wl, wr, scale, handle, _dtype_code(q.dtype),
+                        _dtype_code(o.dtype), _dtype_code(grad_dtype))
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_bwd")
     return dq, dk, dv

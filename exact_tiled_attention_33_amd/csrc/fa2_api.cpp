@@ -177,9 +177,18 @@ int fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o, cons
                 const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int H_kv,
                 int N, int d, int causal, float scale, void* stream, int in_dtype, int o_dtype,
                 int grad_dtype) {
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  return fa2_bwd_window(q, k, v, o, dout, lse, delta, dq, dk, dv, B, H, H_kv, N, d, -1, causal ? 0 : -1,
+                        scale, stream, in_dtype, o_dtype, grad_dtype);
+}
+
+int fa2_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int H_kv,
+                   int N, int d, int window_left, int window_right, float scale, void* stream,
+                   int in_dtype, int o_dtype, int grad_dtype) {
   if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return FA2_ERR_INVALID_ARG;
   if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1) return FA2_ERR_INVALID_ARG;
   if (!is_dtype(o_dtype) || !is_dtype(grad_dtype)) return FA2_ERR_INVALID_ARG;
   const int st = check_sizes(B, H, N, d, in_dtype);
   if (st != FA2_OK) return st;
@@ -213,7 +222,10 @@ int fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o, cons
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.Hkv = H_kv;
-  a.causal = causal != 0;
+  // a bound of N or more keys is no bound
+  a.wl = window_left >= N ? -1 : window_left;
+  a.wr = window_right >= N ? -1 : window_right;
+  a.causal = (a.wl == -1 && a.wr == 0);
   a.scale = scale;
   a.o_bf16 = (o_dtype == FA2_BF16);
   a.grad_bf16 = (grad_dtype == FA2_BF16);

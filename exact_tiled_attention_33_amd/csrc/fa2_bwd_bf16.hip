@@ -208,12 +208,12 @@ constexpr int kSlotBytes = 2 * kQBBytes + 2 * 256;     // Q, dO, LSE row, D row
 constexpr int kKVLds = 2 * kKVTileBytes + 4 * kSlotBytes;  // 2 groups x 2 slots
 static_assert(kKVLds >= 4 * 128 * 64 * 4, "partial sums of one group must fit in LDS");
 
-template <bool CAUSAL, bool GRAD_BF16>
+template <bool MASKED, bool GRAD_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kKVWaves * 64, kKVWaves * 64), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                      const __bf16* __restrict__ dout, const float* __restrict__ lse,
                      const float* __restrict__ delta, void* __restrict__ dk, void* __restrict__ dv,
-                     int BHkv, int N, float c, float scale, int group) {
+                     int BHkv, int N, float c, float scale, int group, int wl, int wr) {
   __shared__ __attribute__((aligned(1024))) char smem[kKVLds];
   const char* const lds_k = smem;
   const char* const lds_v = smem + kKVTileBytes;
@@ -235,6 +235,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const long long head = (long long)bkv * N * kD;  // K, V, dK, dV
   const int kw0 = k0 + 32 * gw;  // first key of this wave
   const int key = kw0 + l32;     // this lane's key
+  // Key j is visible to query i iff i - wl <= j <= i + wr (-1: no limit on
+  // that side; causal: wl = -1, wr = 0).  This lane's key is seen by the
+  // queries [q_lo, q_hi] (empty past N): the mask is two compares.
+  const int q_lo = (MASKED && wr >= 0) ? max(0, key - wr) : 0;
+  const int q_hi = key >= N ? -1 : ((MASKED && wl >= 0) ? min(N - 1, key + wl) : N - 1);
 
   // ---- K and V tiles (once): 32 copy instructions each, 4 per wave ----
   {
@@ -254,8 +259,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // The work is the list of (query head, block) pairs, query head major;
   // step s of wave group grp takes item 2s + grp.
   const int nqb = (N + kQB - 1) / kQB;
-  const int b_first = CAUSAL ? k0 / kQB : 0;
-  const int nb = nqb - b_first;  // blocks per query head
+  // query blocks holding a query that sees a key of this tile
+  const int b_first = (MASKED && wr >= 0) ? max(0, k0 - wr) / kQB : 0;
+  const int b_last = (MASKED && wl >= 0) ? min(N - 1, min(k0 + kKVKeys, N) - 1 + wl) / kQB : nqb - 1;
+  const int nb = b_last - b_first + 1;  // blocks per query head
   const int n_items = group * nb;
   const int n_steps = (n_items + 1) / 2;
   // group-local copy of item it into ring slot `slot`: Q and dO 8
@@ -326,8 +333,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       const bf16x8 vb = *(const bf16x8*)(lds_v + krw[s]);
       dpacc = mfma(ga, vb, dpacc);
     }
-    // P and dS.  Causal diagonal blocks and ragged edges are masked (P = 0).
-    const bool edge = (CAUSAL && q0 < kw0 + 32) || q0 + kQB > N || kw0 + 32 > N;
+    // P and dS.  Blocks not wholly inside every key's band (and ragged
+    // edges) are masked (P = 0).
+    const bool edge = (MASKED && ((wr >= 0 && q0 < kw0 + 31 - wr) || (wl >= 0 && q0 + 31 > kw0 + wl))) ||
+                      q0 + kQB > N || kw0 + 32 > N;
     float p[16], ds[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -339,8 +348,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         float pi = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -l4[r] * kLog2e));
         if (edge) {
           const int qq = q0 + 8 * g + 4 * half + r;
-          const bool vis = qq < N && key < N && (!CAUSAL || key <= qq);
-          pi = vis ? pi : 0.f;
+          pi = (qq >= q_lo) & (qq <= q_hi) ? pi : 0.f;
         }
         p[i] = pi;
         ds[i] = pi * (dpacc[i] - d4[r]);
@@ -388,8 +396,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int it = 2 * s + grp;
     if (it + 2 < n_items) copy_block(it + 2, kSl ^ 1);
     const int b = b_first + it % nb;
-    // a block lying wholly above this wave's keys (causal) contributes 0
-    if (it < n_items && !(CAUSAL && b * kQB + kQB <= kw0)) compute(b, slot_c);
+    // a block with no query that sees one of this wave's keys contributes 0
+    const bool outside = MASKED && ((wr >= 0 && b * kQB + kQB - 1 < kw0 - wr) ||
+                                    (wl >= 0 && b * kQB > kw0 + 31 + wl));
+    if (it < n_items && !outside) compute(b, slot_c);
     wait_vmem(0);
     __syncthreads();
   };
@@ -449,12 +459,12 @@ constexpr int kQTileBytes = kQCols * kRowBytes;  // 16 KiB (K or V)
 constexpr int kQStage = 2 * kQTileBytes;         // K then V
 constexpr int kQRing = 3;
 
-template <bool CAUSAL, bool GRAD_BF16>
+template <bool MASKED, bool GRAD_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kQWaves * 64, kQWaves * 64), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                    const __bf16* __restrict__ dout, const float* __restrict__ lse,
                    const float* __restrict__ delta, void* __restrict__ dq, int BH, int N, int T, float c,
-                   float scale, int group) {
+                   float scale, int group, int wl, int wr) {
   __shared__ __attribute__((aligned(1024))) char smem[kQRing * kQStage];
 
   const int lane = threadIdx.x & 63;
@@ -463,7 +473,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
 
   const int bh = blockIdx.x % BH;
   const int tr = blockIdx.x / BH;
-  const int t = CAUSAL ? (T - 1 - tr) : tr;
+  const int t = MASKED ? (T - 1 - tr) : tr;
   const long long head = (long long)bh * N * kD;
   // grouped key/value heads: `group` consecutive query heads share one
   const long long kv_head = (long long)(bh / group) * N * kD;
@@ -487,20 +497,38 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
   const float nlse2 = qrow < N ? -lse[(long long)bh * N + qrow] * kLog2e : 0.f;
   const float dlt = qrow < N ? delta[(long long)bh * N + qrow] : 0.f;
 
+  // Key tiles streamed: j_lo .. j_lo + n_tiles - 1 (those with a key some
+  // row of the workgroup sees); this wavefront computes on jw_lo .. jw_hi-1
+  // and needs no mask on jf_lo .. jf_hi-1 (keys below N that all its rows
+  // see).  Key j is visible to query i iff i - wl <= j <= i + wr.
   const int nk = (N + kQCols - 1) / kQCols;
-  int n_tiles = nk, n_w = (qw < N) ? nk : 0, n_full = N / kQCols;
-  if (CAUSAL) {
-    n_tiles = min(nk, (min(q0 + kQRows, N) - 1) / kQCols + 1);
-    n_w = (qw < N) ? min(nk, (min(qw + 32, N) - 1) / kQCols + 1) : 0;
-    n_full = min(n_full, (qw + 1) / kQCols);
+  int j_lo = 0, n_tiles = nk, jw_lo = 0, jw_hi = (qw < N) ? nk : 0, jf_lo = 0, jf_hi = N / kQCols;
+  if (MASKED) {
+    const int q_last = min(q0 + kQRows, N) - 1;
+    const int w_last = min(qw + 32, N) - 1;
+    int j_hi = nk;
+    if (wl >= 0) {
+      j_lo = max(0, q0 - wl) / kQCols;
+      jw_lo = max(0, qw - wl) / kQCols;
+      jf_lo = (max(0, w_last - wl) + kQCols - 1) / kQCols;
+    }
+    if (wr >= 0) {
+      j_hi = min(nk, (q_last + wr) / kQCols + 1);
+      jw_hi = (qw < N) ? min(nk, (w_last + wr) / kQCols + 1) : 0;
+      jf_hi = min(jf_hi, qw + wr - (kQCols - 1) >= 0 ? (qw + wr - (kQCols - 1)) / kQCols + 1 : 0);
+    }
+    n_tiles = j_hi - j_lo;
   }
+  // this row's visible keys [key_lo, key_hi]
+  const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
+  const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
 
   const LdsOffsets off = lds_offsets(lane);
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset_of(smem));
   // tile copies: 16 instructions for K and 16 for V; instruction i is
   // issued by wave i % 8
   auto copy_tile = [&](int j) __attribute__((always_inline)) {
-    const int key0 = j * kQCols;
+    const int key0 = (j_lo + j) * kQCols;
     const int rows = min(kQCols, N - key0);
     const i32x4 rk = raw_rsrc(k + kv_head + (long long)key0 * kD, rows * kRowBytes);
     const i32x4 rv = raw_rsrc(v + kv_head + (long long)key0 * kD, rows * kRowBytes);
@@ -529,7 +557,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
       for (int u = 0; u < 2; ++u) ktr[db][u] = pin(off.tr[db][u] + sbase);
-    const bool edge = j >= n_full;
+    const int ja = j_lo + j;  // key tile index
+    const bool edge = ja < jf_lo || ja >= jf_hi;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T for keys 32*kb .. +31 of the tile,
@@ -548,9 +577,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
       for (int i = 0; i < 16; ++i) {
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, nlse2));
         if (edge) {
-          const int kk = j * kQCols + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool vis = kk < N && (!CAUSAL || kk <= qrow);
-          p = vis ? p : 0.f;
+          const int kk = ja * kQCols + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          p = (kk >= key_lo) & (kk <= key_hi) ? p : 0.f;
         }
         ds[i] = p * (dpacc[i] - dlt);
       }
@@ -581,7 +609,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
     wait_vmem(j + 1 < n_tiles ? kCopies : 0);
     __syncthreads();
     if (j + 2 < n_tiles) copy_tile(j + 2);
-    if (j < n_w) compute(j);
+    if (j_lo + j >= jw_lo && j_lo + j < jw_hi) compute(j);
   }
 
   if (qrow >= N) return;
@@ -602,7 +630,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
     }
 }
 
-template <bool CAUSAL, bool GRAD_BF16>
+template <bool MASKED, bool GRAD_BF16>
 hipError_t launch_bwd_t(const BwdArgs& a, float c) {
   const int BH = a.B * a.H;
   const int BHkv = a.B * a.Hkv;
@@ -611,14 +639,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, float c) {
   const int T = (a.N + kQRows - 1) / kQRows;
   const long long q_grid = (long long)T * BH;
   if (kv_grid > 0x7fffffffLL || q_grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL, GRAD_BF16>), dim3((unsigned)kv_grid), dim3(kKVWaves * 64), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<MASKED, GRAD_BF16>), dim3((unsigned)kv_grid), dim3(kKVWaves * 64), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                     a.delta, a.dk, a.dv, BHkv, a.N, c, a.scale, group);
+                     a.delta, a.dk, a.dv, BHkv, a.N, c, a.scale, group, a.wl, a.wr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL, GRAD_BF16>), dim3((unsigned)q_grid), dim3(kQWaves * 64), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<MASKED, GRAD_BF16>), dim3((unsigned)q_grid), dim3(kQWaves * 64), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                     a.delta, a.dq, BH, a.N, T, c, a.scale, group);
+                     a.delta, a.dq, BH, a.N, T, c, a.scale, group, a.wl, a.wr);
   return hipGetLastError();
 }
 
@@ -638,7 +666,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
-  if (a.causal) return a.grad_bf16 ? launch_bwd_t<true, true>(a, c) : launch_bwd_t<true, false>(a, c);
+  if (a.wl >= 0 || a.wr >= 0) return a.grad_bf16 ? launch_bwd_t<true, true>(a, c) : launch_bwd_t<true, false>(a, c);
   return a.grad_bf16 ? launch_bwd_t<false, true>(a, c) : launch_bwd_t<false, false>(a, c);
 }
 

@@ -50,6 +50,7 @@ struct BwdArgs {
   int B, H, N, d;
   int Hkv;  // key/value heads (H for ordinary multi-head attention)
   bool causal;
+  int wl, wr;  // sliding window, as in FwdArgs
   float scale;
   bool o_bf16;
   bool grad_bf16;

@@ -214,6 +214,19 @@ int fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o, cons
                 void* stream, int in_dtype, int o_dtype, int grad_dtype);
 
 /*
+ * fa2_bwd_window -- fa2_bwd_gqa under a sliding-window mask (see
+ * fa2_fwd_window for the bounds).  o and lse must come from fa2_fwd_window
+ * with the same bounds.  fa2_bwd_gqa(..., causal, ...) is fa2_bwd_window
+ * with (-1, causal ? 0 : -1).  Key tiles (dQ) and query blocks (dK, dV)
+ * wholly outside the band are skipped.  Returns FA2_OK after enqueueing,
+ * else a negative fa2_status (window bounds below -1: FA2_ERR_INVALID_ARG).
+ */
+int fa2_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, float* delta, void* dq, void* dk, void* dv,
+                   int B, int H, int H_kv, int N, int d, int window_left, int window_right,
+                   float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype);
+
+/*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,
  * for reporting and tests.  Host-only; touches no device.
  */

@@ -285,3 +285,19 @@ def test_window_no_device_status_on_cpu_only_host():
     # bounds of N or more are no bounds: fp32 accepts them as no mask / causal
     assert _wcall(64, 0, in_dtype=fa2.F32) == fa2.FA2_ERR_NO_DEVICE
     assert _wcall(1000, 1000, in_dtype=fa2.F32) == fa2.FA2_ERR_NO_DEVICE
+
+
+def _wbcall(wl, wr, **over):
+    a = dict(BGOOD, **over)
+    return fa2.fa2_bwd_window(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["delta"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["H"], a["N"], a["d"], wl, wr, a["scale"],
+                              a["stream"], a["in_dtype"], a["o_dtype"], a["grad_dtype"])
+
+
+def test_bwd_window_validation():
+    assert _wbcall(-2, 0) == fa2.FA2_ERR_INVALID_ARG
+    assert _wbcall(0, -7) == fa2.FA2_ERR_INVALID_ARG
+    assert _wbcall(5, 5, d=64) == fa2.FA2_ERR_UNSUPPORTED
+    if not _gpu_present():
+        assert _wbcall(5, 5) == fa2.FA2_ERR_NO_DEVICE
+        assert _wbcall(-1, 0) == fa2.FA2_ERR_NO_DEVICE

@@ -1,6 +1,7 @@
-"""GPU parity of sliding-window (local) attention: fa2_fwd_window against
-the fp64 oracle, every element, at the forward bars (bf16 inputs:
-|O| <= 1e-2, |LSE| <= 1e-3 with fp32 O).
+"""GPU parity of sliding-window (local) attention: fa2_fwd_window and
+fa2_bwd_window against the fp64 oracles, every element, at the forward bars
+(bf16 inputs: |O| <= 1e-2, |LSE| <= 1e-3 with fp32 O) and the backward one
+(|g - g_ref| <= 2^-6 m + 1e-6 max(m), m the per-element magnitude).
 
 Windows are chosen to land on and around the 64-key tile and 256-row query
 tile edges, one-sided and two-sided, with ragged sequence lengths, d = 64
@@ -17,6 +18,7 @@ import pytest
 import torch
 
 import exact_tiled_attention_33_amd as fa2
+import oracle.attention_grad as gref
 import oracle.exact_attention as ref
 import workloads
 
@@ -87,3 +89,62 @@ def test_window_rejections():
     qf, kf, vf = (t.float() for t in (q, k, v))
     with pytest.raises(fa2.Fa2Error):
         fa2.forward(qf, kf, vf, window=(10, 0))   # fp32: no mask or causal only
+
+
+# --- backward under a sliding window ------------------------------------------
+
+BWD = [
+    # B, H, H_kv, N, window_left, window_right, outliers
+    (1, 2, 2, 700, 63, 0, True),
+    (1, 1, 1, 600, 100, 50, False),
+    (1, 2, 1, 513, 77, 0, False),
+    (1, 1, 1, 1000, 128, 128, False),
+    (1, 1, 1, 600, -1, 100, False),
+    (1, 1, 1, 600, 300, -1, True),
+    (2, 4, 2, 300, 31, 5, False),
+    (1, 1, 1, 200, 0, 0, False),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,wl,wr,outliers", BWD,
+                         ids=[f"{b}x{h}/{hk}x{n}-w({l},{r})" for b, h, hk, n, l, r, _ in BWD])
+def test_window_backward_every_element(B, H, H_kv, N, wl, wr, outliers):
+    q, k, v = _inputs(B, H, H_kv, N, 128, seed=900 + N + wl, outliers=outliers)
+    w = workloads.get("long_causal").with_(B=B, H=H, N=N)
+    g = workloads.make_grad_output(w, 901 + N)
+    scale = 1.0 / math.sqrt(128)
+    print(f"[case] window bwd {B}x{H}/{H_kv}x{N} window=({wl},{wr})", flush=True)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa2.forward(qd, kd, vd, scale=scale, window=(wl, wr))
+    dq, dk, dv = fa2.backward(qd, kd, vd, o, lse, gd, scale=scale, window=(wl, wr))
+    torch.cuda.synchronize()
+    Q, K, V, G = (_np64(t) for t in (q, k, v, g))
+    refs = gref.attention_grad_ref_window(Q, K, V, G, scale, wl, wr)
+    mq, mk, mv = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    group = H // H_kv
+    for b in range(B):
+        for h in range(H):
+            gk = h // group
+            a, bb, c = gref.grad_magnitudes_head_window(Q[b, h], K[b, gk], V[b, gk], G[b, h], scale, wl, wr)
+            mq[b, h] = a
+            mk[b, gk] += bb
+            mv[b, gk] += c
+    for name, x, r, m in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, (mq, mk, mv)):
+        x = _np64(x)
+        assert np.all(np.isfinite(x)), name
+        err = np.abs(x - r)
+        ratio = float(np.max(err / np.maximum(m, 1e-30)))
+        print(f"[window bwd] {name}: max|err|={float(np.max(err)):.3e} max err/m={ratio:.2e}", flush=True)
+        assert np.all(err <= 2.0 ** -6 * m + 1e-6 * float(np.max(m))), f"{name} exceeds the bound"
+
+
+def test_causal_window_backward_is_bitwise_the_causal_backward():
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 2, 640, 128, seed=14, outliers=True))
+    g = workloads.make_grad_output(workloads.get("long_causal").with_(B=1, H=2, N=640), 15).to(DEV)
+    print("[case] window bwd (-1,0) vs causal", flush=True)
+    o, lse = fa2.forward(q, k, v, causal=True, scale=0.09)
+    a = fa2.backward(q, k, v, o, lse, g, causal=True, scale=0.09)
+    b = fa2.backward(q, k, v, o, lse, g, scale=0.09, window=(-1, 0))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
