@@ -21,6 +21,10 @@ With --kv-heads K (K dividing H) the key/value tensors have K heads and the
 grouped-head entry points run (fa2_fwd_gqa / fa2_bwd_gqa); the credited work
 is unchanged (it counts query heads).
 
+With --window LEFT RIGHT the sliding-window entry points run
+(fa2_fwd_window / fa2_bwd_window) and the credited work counts only the
+visible (query, key) pairs: 4*d (forward) or 10*d (backward) flop per pair.
+
 With --pass bwd a step is one fa2_bwd call (the D, dK/dV and dQ kernels) on
 the same workload, with dO drawn from the seeded generator and O and LSE
 from one fa2_fwd call made before timing; throughput is credited backward
@@ -126,6 +130,17 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
     }
 
 
+def window_of(args, w):
+    """(window_left, window_right) of the run: --window, else the workload's
+    causal (-1, 0) or unmasked (-1, -1) form."""
+    if args.window is not None:
+        wl, wr = args.window
+        if wl < -1 or wr < -1:
+            raise SystemExit("bench.py: --window bounds must be >= -1")
+        return wl, wr
+    return (-1, 0) if w.causal else (-1, -1)
+
+
 def kv_heads(args, w) -> int:
     """Key/value heads of the run: --kv-heads if given (grouped heads), else H."""
     hkv = args.kv_heads or w.H
@@ -154,12 +169,13 @@ def run_bench(args) -> dict:
     in_code = fa2.BF16 if w.dtype == "bf16" else fa2.F32
     o_code = fa2.BF16 if args.o_dtype == "bf16" else fa2.F32
     handle = stream.cuda_stream
+    wl, wr = window_of(args, w)
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 w.B, w.H, hkv, w.N, w.d, int(w.causal), w.scale, handle, in_code, o_code)
+                 w.B, w.H, hkv, w.N, w.d, wl, wr, w.scale, handle, in_code, o_code)
     torch.cuda.synchronize()
 
     def step():
-        st = fa2.fa2_fwd_gqa(*call_args)
+        st = fa2.fa2_fwd_window(*call_args)
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st)
 
@@ -181,10 +197,11 @@ def run_bench(args) -> dict:
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     span_ms = starts[0].elapsed_time(ends[-1])
 
-    flops = workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal)
+    flops = (workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal) if args.window is None
+             else 4.0 * w.B * w.H * w.d * workloads.credited_pairs(w.N, wl, wr))
     value = flops * args.steps / wall / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = traffic_from_profiles(w.name) if hkv == w.H else None
+    traffic = traffic_from_profiles(w.name) if hkv == w.H and args.window is None else None
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
     # Algorithmic bytes per launch: Q, K, V read once, O and LSE written once.
     esz = 2 if w.dtype == "bf16" else 4
@@ -218,6 +235,7 @@ def run_bench(args) -> dict:
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
             "scale": w.scale, "in_dtype": w.dtype, "o_dtype": args.o_dtype, "kv_heads": hkv,
+            "window": [wl, wr],
             "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
             "dropout": 0.0, "backward": False, "parallelism": "single GPU",
         },
@@ -241,7 +259,7 @@ def run_bench(args) -> dict:
         "kernel_source_sha256_16": kernel_source_hash(),
         "context_not_target": "pages (A100): FA1 25-40% of peak, FA2 50-73% of peak, up to 230 TFLOP/s",
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.window is None:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, budget_s=args.cpu_budget)
     return result
 
@@ -301,18 +319,19 @@ def run_bench_bwd(args) -> dict:
     k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     g = workloads.make_grad_output(w, seed=args.seed + 7919, device=dev)
     stream = torch.cuda.Stream(device=dev)
+    wl, wr = window_of(args, w)
     with torch.cuda.stream(stream):
-        o, lse = fa2.forward(q, k, v, causal=w.causal, scale=w.scale, stream=stream)
+        o, lse = fa2.forward(q, k, v, scale=w.scale, stream=stream, window=(wl, wr))
     delta = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
     dq = torch.empty(w.shape, dtype=torch.float32, device=dev)
     dk, dv = (torch.empty(k.shape, dtype=torch.float32, device=dev) for _ in range(2))
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
                  delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, hkv, w.N, w.d,
-                 int(w.causal), w.scale, stream.cuda_stream, fa2.BF16, fa2.F32, fa2.F32)
+                 wl, wr, w.scale, stream.cuda_stream, fa2.BF16, fa2.F32, fa2.F32)
     torch.cuda.synchronize()
 
     def step():
-        st = fa2.fa2_bwd_gqa(*call_args)
+        st = fa2.fa2_bwd_window(*call_args)
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st, "fa2_bwd")
 
@@ -330,9 +349,10 @@ def run_bench_bwd(args) -> dict:
     wall = time.perf_counter() - t0
     per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(per_call_ms) / len(per_call_ms)
-    flops = workloads.credited_bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    pairs = workloads.credited_pairs(w.N, wl, wr)
+    flops = 10.0 * w.B * w.H * w.d * pairs
     # executed: dK/dV recomputes S and dP (4 products), dQ does S, dP, dQ (3)
-    executed = 14.0 * w.B * w.H * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    executed = 14.0 * w.B * w.H * w.d * pairs
     value = flops * args.steps / wall / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     result = {
@@ -351,6 +371,7 @@ def run_bench_bwd(args) -> dict:
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
             "scale": w.scale, "in_dtype": w.dtype, "o_dtype": "fp32", "grad_dtype": "fp32", "kv_heads": hkv,
+            "window": [wl, wr],
             "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
             "dropout": 0.0, "backward": True, "parallelism": "single GPU",
         },
@@ -373,7 +394,7 @@ def run_bench_bwd(args) -> dict:
                 "cus": props.multi_processor_count},
         "kernel_source_sha256_16": kernel_source_hash(BWD_SOURCES),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.window is None:
         result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, g, budget_s=args.cpu_budget)
     return result
 
@@ -422,6 +443,9 @@ def main() -> int:
     ap.add_argument("--o-dtype", choices=["fp32", "bf16"], default="fp32")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="fwd (default): the forward pass; bwd: the backward pass")
+    ap.add_argument("--window", type=int, nargs=2, default=None, metavar=("LEFT", "RIGHT"),
+                    help="sliding-window mask: key j visible to query i iff i-LEFT <= j <= i+RIGHT "
+                         "(-1 = unbounded side); overrides the workload's causal flag")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="key/value heads (grouped heads; default: as many as query heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

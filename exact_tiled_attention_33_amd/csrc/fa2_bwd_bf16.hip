@@ -337,6 +337,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // edges) are masked (P = 0).
     const bool edge = (MASKED && ((wr >= 0 && q0 < kw0 + 31 - wr) || (wl >= 0 && q0 + 31 > kw0 + wl))) ||
                       q0 + kQB > N || kw0 + 32 > N;
+    if (edge) {
+      // a real branch: blocks inside every key's band skip the mask (the
+      // empty volatile statement keeps the compiler from applying it to
+      // every block as selects)
+      asm volatile("");
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qq = q0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        sacc[i] = (qq >= q_lo) & (qq <= q_hi) ? sacc[i] : -INFINITY;
+      }
+    }
     float p[16], ds[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -345,11 +356,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
-        float pi = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -l4[r] * kLog2e));
-        if (edge) {
-          const int qq = q0 + 8 * g + 4 * half + r;
-          pi = (qq >= q_lo) & (qq <= q_hi) ? pi : 0.f;
-        }
+        const float pi = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -l4[r] * kLog2e));
         p[i] = pi;
         ds[i] = pi * (dpacc[i] - d4[r]);
       }
@@ -572,14 +579,21 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
         const bf16x8 va = *(const bf16x8*)(smem + krow[s] + kQTileBytes + 32 * kb * kRowBytes);
         dpacc = mfma(va, gf[s], dpacc);
       }
+      if (edge) {
+        // a real branch: tiles inside every row's band skip the mask (the
+        // empty volatile statement keeps the compiler from applying it to
+        // every tile as selects)
+        asm volatile("");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = ja * kQCols + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          sacc[i] = (kk >= key_lo) & (kk <= key_hi) ? sacc[i] : -INFINITY;
+        }
+      }
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, nlse2));
-        if (edge) {
-          const int kk = ja * kQCols + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          p = (kk >= key_lo) & (kk <= key_hi) ? p : 0.f;
-        }
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i], c, nlse2));
         ds[i] = p * (dpacc[i] - dlt);
       }
       bf16x8 dsk[2];

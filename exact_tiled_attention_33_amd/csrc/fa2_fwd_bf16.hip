@@ -482,6 +482,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto vector_phase = [&](int j) __attribute__((always_inline)) {
     const int ja = j_lo + j;  // key tile index
     if (ja < jf_lo || ja >= jf_hi) {
+      // a real branch: tiles inside every row's band skip the mask (the
+      // empty volatile statement keeps the compiler from applying it to
+      // every tile as selects)
+      asm volatile("");
       // element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*half + (i%4)
       const int key0 = ja * kBc;
 #pragma unroll

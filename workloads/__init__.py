@@ -32,7 +32,7 @@ from dataclasses import dataclass, replace
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "HEADLINE", "make_inputs", "make_grad_output", "credited_flops",
-           "credited_bwd_flops", "get"]
+           "credited_bwd_flops", "credited_pairs", "get"]
 
 
 @dataclass(frozen=True)
@@ -120,6 +120,17 @@ def credited_bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     halved when causal."""
     f = 10.0 * B * H * N * N * d
     return f / 2.0 if causal else f
+
+
+def credited_pairs(N: int, window_left: int, window_right: int) -> int:
+    """Number of (query, key) pairs of one head that a sliding window
+    (-1 = unbounded side) leaves visible: sum over queries i of the keys j
+    with max(0, i - wl) <= j <= min(N - 1, i + wr).  (-1, 0) gives the
+    causal N(N+1)/2, (-1, -1) gives N^2."""
+    i = torch.arange(N, dtype=torch.int64)
+    lo = torch.clamp(i - window_left, min=0) if window_left >= 0 else torch.zeros_like(i)
+    hi = torch.clamp(i + window_right, max=N - 1) if window_right >= 0 else torch.full_like(i, N - 1)
+    return int((hi - lo + 1).clamp(min=0).sum())
 
 
 def credited_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
