@@ -25,6 +25,14 @@ With --window LEFT RIGHT the sliding-window entry points run
 (fa2_fwd_window / fa2_bwd_window) and the credited work counts only the
 visible (query, key) pairs: 4*d (forward) or 10*d (backward) flop per pair.
 
+By default (--split auto) the forward asks fa2_split_plan for a schedule on
+the device's compute units: where the grid of query tiles is too small and
+uneven to fill the chip (few heads, long sequences, causal), heavy tiles'
+key ranges are cut into chunks and a step is fa2_fwd_split (the forward
+kernel over the chunks, then the merge of the partial results); otherwise
+a step is fa2_fwd_window.  --split off always runs fa2_fwd_window.  Events
+bracket the whole step, so with a split the kernel time includes the merge.
+
 With --pass bwd a step is one fa2_bwd call (the D, dK/dV and dQ kernels) on
 the same workload, with dO drawn from the seeded generator and O and LSE
 from one fa2_fwd call made before timing; throughput is credited backward
@@ -172,10 +180,23 @@ def run_bench(args) -> dict:
     wl, wr = window_of(args, w)
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  w.B, w.H, hkv, w.N, w.d, wl, wr, w.scale, handle, in_code, o_code)
+    schedule = {"split": False}
+    if args.split == "auto" and w.dtype == "bf16":
+        splan = fa2.split_plan(w.shape, window=(wl, wr), num_units=props.multi_processor_count)
+        if splan.splits:
+            items = splan.device_items(dev)
+            workspace = torch.empty(splan.workspace_bytes, dtype=torch.uint8, device=dev)
+            call_args = call_args + (items.data_ptr(), splan.n_items, splan.n_slots, workspace.data_ptr(),
+                                     splan.workspace_bytes)
+            lengths = splan.items[:, 2] - splan.items[:, 1]
+            schedule = {"split": True, "items": splan.n_items, "partial_slots": splan.n_slots,
+                        "workgroups": splan.n_items * w.B * w.H, "longest_chunk_key_tiles": int(lengths.max()),
+                        "workspace_bytes": splan.workspace_bytes}
+    fwd_call = fa2.fa2_fwd_split if schedule["split"] else fa2.fa2_fwd_window
     torch.cuda.synchronize()
 
     def step():
-        st = fa2.fa2_fwd_window(*call_args)
+        st = fwd_call(*call_args)
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st)
 
@@ -201,7 +222,8 @@ def run_bench(args) -> dict:
              else 4.0 * w.B * w.H * w.d * workloads.credited_pairs(w.N, wl, wr))
     value = flops * args.steps / wall / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = traffic_from_profiles(w.name) if hkv == w.H and args.window is None else None
+    traffic = (traffic_from_profiles(w.name) if hkv == w.H and args.window is None and not schedule["split"]
+               else None)
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
     # Algorithmic bytes per launch: Q, K, V read once, O and LSE written once.
     esz = 2 if w.dtype == "bf16" else 4
@@ -239,6 +261,7 @@ def run_bench(args) -> dict:
             "outlier_frac": w.outlier_frac, "outlier_mult": w.outlier_mult, "seed": args.seed,
             "dropout": 0.0, "backward": False, "parallelism": "single GPU",
         },
+        "schedule": schedule,
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
             **roof,
@@ -448,6 +471,8 @@ def main() -> int:
                          "(-1 = unbounded side); overrides the workload's causal flag")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="key/value heads (grouped heads; default: as many as query heads)")
+    ap.add_argument("--split", choices=["auto", "off"], default="auto",
+                    help="forward: split heavy query tiles' key ranges when the planner predicts a gain")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--calibrate-copy", action="store_true")

@@ -13,6 +13,10 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_fwd_window / fa2_bwd_window: the *_gqa calls with (window_left, window_right)
         instead of causal (sliding-window mask)
     fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units=0) -> dict
+    fa2_split_plan(B, H, N, d, window_left, window_right, in_dtype, num_units, max_chunk_tiles=0)
+        -> SplitPlan (host schedule; key ranges of heavy query tiles cut into chunks)
+    fa2_fwd_split(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, scale, stream,
+        in_dtype, o_dtype, items, n_items, n_slots, workspace, workspace_bytes) -> int
     fa2_strerror(status) -> str
     fa2_version() -> int
 Convenience wrappers over torch device tensors (k and v may have fewer heads
@@ -20,6 +24,8 @@ than q: grouped key/value heads):
     forward(q, k, v, causal=False, scale=None, o_dtype=torch.float32) -> (o, lse)
     backward(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=torch.float32)
         -> (dq, dk, dv)
+    split_plan(q_shape, causal=False, window=None, num_units=None, max_chunk_tiles=0) -> SplitPlan
+    forward_split(q, k, v, plan, causal=False, scale=None, ...) -> (o, lse)
 """
 
 from __future__ import annotations
@@ -33,6 +39,7 @@ __all__ = [
     "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
     "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
     "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "fa2_bwd_window", "forward", "backward",
+    "fa2_split_plan", "fa2_fwd_split", "SplitPlan", "split_plan", "forward_split",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -46,7 +53,8 @@ FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
-                    "fa2_bwd_window", "fa2_plan", "fa2_strerror", "fa2_version")
+                    "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_strerror",
+                    "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -56,6 +64,45 @@ class Fa2Error(RuntimeError):
     def __init__(self, status: int, where: str = "fa2_fwd"):
         self.status = status
         super().__init__(f"{where} failed with status {status}: {fa2_strerror(status)}")
+
+
+class _SplitItem(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int) for name in ("tile", "kt_lo", "kt_hi", "slot", "slot0", "n_parts")]
+
+
+class SplitPlan:
+    """A split forward schedule from fa2_split_plan.
+
+    ``items`` is an int32 array [n_items, 6] with the columns of
+    fa2_split_item (tile, kt_lo, kt_hi, slot, slot0, n_parts); ``n_slots``
+    and ``workspace_bytes`` are what fa2_fwd_split needs.  ``shape`` and
+    ``window`` record what the schedule was built for.
+    """
+
+    def __init__(self, items, n_slots: int, workspace_bytes: int, shape, window):
+        self.items = items
+        self.n_slots = int(n_slots)
+        self.workspace_bytes = int(workspace_bytes)
+        self.shape = tuple(shape)
+        self.window = tuple(window)
+        self._dev = {}
+
+    @property
+    def n_items(self) -> int:
+        return int(self.items.shape[0])
+
+    @property
+    def splits(self) -> bool:
+        return self.n_slots > 0
+
+    def device_items(self, device):
+        """The schedule as an int32 device tensor (copied once per device)."""
+        import torch
+
+        key = str(device)
+        if key not in self._dev:
+            self._dev[key] = torch.from_numpy(self.items).to(device)
+        return self._dev[key]
 
 
 class _Plan(ctypes.Structure):
@@ -133,6 +180,19 @@ def load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_Plan),
     ]
+    lib.fa2_split_plan.restype = ctypes.c_int
+    lib.fa2_split_plan.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t),
+    ]
+    lib.fa2_fwd_split.restype = ctypes.c_int
+    lib.fa2_fwd_split.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+    ]
     lib.fa2_strerror.restype = ctypes.c_char_p
     lib.fa2_strerror.argtypes = [ctypes.c_int]
     lib.fa2_version.restype = ctypes.c_int
@@ -189,6 +249,33 @@ def fa2_plan(B, H, N, d, causal, in_dtype, block_rows=0, block_cols=0, num_units
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_plan")
     return {name: getattr(out, name) for name, _ in _Plan._fields_}
+
+
+def fa2_split_plan(B, H, N, d, window_left, window_right, in_dtype, num_units, max_chunk_tiles=0) -> SplitPlan:
+    """Raw C call (two passes: count, then fill); raises Fa2Error on a bad status."""
+    import numpy as np
+
+    lib = load()
+    n_items, n_slots, ws = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_size_t(0)
+    args = (B, H, N, d, int(window_left), int(window_right), in_dtype, int(num_units), int(max_chunk_tiles))
+    st = int(lib.fa2_split_plan(*args, None, 0, ctypes.byref(n_items), ctypes.byref(n_slots), ctypes.byref(ws)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_split_plan")
+    buf = (_SplitItem * max(1, n_items.value))()
+    st = int(lib.fa2_split_plan(*args, ctypes.cast(buf, ctypes.c_void_p), n_items.value, ctypes.byref(n_items),
+                                ctypes.byref(n_slots), ctypes.byref(ws)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_split_plan")
+    items = np.frombuffer(buf, dtype=np.int32, count=6 * n_items.value).reshape(n_items.value, 6).copy()
+    return SplitPlan(items, n_slots.value, ws.value, (B, H, N, d), (window_left, window_right))
+
+
+def fa2_fwd_split(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, scale, stream, in_dtype,
+                  o_dtype, items, n_items, n_slots, workspace, workspace_bytes) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_fwd_split(q, k, v, o, lse, B, H, H_kv, N, d, int(window_left), int(window_right),
+                                    float(scale), stream, in_dtype, o_dtype, items, int(n_items), int(n_slots),
+                                    workspace, int(workspace_bytes)))
 
 
 def fa2_strerror(status: int) -> str:
@@ -309,3 +396,63 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_bwd")
     return dq, dk, dv
+
+
+def split_plan(q_shape, causal: bool = False, window=None, num_units: int | None = None,
+               max_chunk_tiles: int = 0) -> SplitPlan:
+    """fa2_split_plan for a [B, H, N, d] bf16 query; ``num_units`` defaults
+    to the current device's compute-unit count."""
+    B, H, N, d = q_shape
+    wl, wr = (-1, 0 if causal else -1) if window is None else window
+    if num_units is None and max_chunk_tiles == 0:
+        import torch
+
+        num_units = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return fa2_split_plan(B, H, N, d, wl, wr, BF16, num_units or 0, max_chunk_tiles)
+
+
+def forward_split(q, k, v, plan: SplitPlan, causal: bool = False, scale: float | None = None, o_dtype=None,
+                  out=None, lse=None, stream=None, window=None, workspace=None):
+    """Attention forward over a split schedule (fa2_fwd_split); returns (o, lse).
+
+    Arguments as ``forward``; ``plan`` comes from ``split_plan`` for the same
+    shape and mask.  ``workspace`` (a device uint8 tensor of at least
+    ``plan.workspace_bytes``) is allocated here when not given.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    wl, wr = (-1, 0 if causal else -1) if window is None else window
+    if plan.shape != (B, H, N, d) or plan.window != (wl, wr):
+        raise ValueError(f"plan was built for {plan.shape} window {plan.window}, not {tuple(q.shape)} ({wl}, {wr})")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of o_dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if workspace is None and plan.workspace_bytes > 0:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    items = plan.device_items(q.device)
+    st = fa2_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                       k.shape[1], N, d, wl, wr, scale, handle, _dtype_code(q.dtype), _dtype_code(o_dtype),
+                       items.data_ptr(), plan.n_items, plan.n_slots, ws_ptr, ws_bytes)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_fwd_split")
+    return out, lse

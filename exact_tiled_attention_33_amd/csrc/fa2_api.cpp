@@ -7,7 +7,11 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
+#include <functional>
+#include <queue>
+#include <vector>
 
 #include "fa2_launch.h"
 
@@ -41,6 +45,142 @@ void own_tiles(int in_dtype, int* rows, int* cols, int* waves) {
   } else {
     *rows = fa2::kF32BlockRows; *cols = fa2::kF32BlockCols; *waves = fa2::kF32Waves;
   }
+}
+
+// Validation shared by the forward entry points; fills *a on success.
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                int d, int window_left, int window_right, float scale, void* stream, int in_dtype, int o_dtype,
+                fa2::FwdArgs* a) {
+  if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1) return FA2_ERR_INVALID_ARG;
+  if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
+  if (!is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
+  const int st = check_sizes(B, H, N, d, in_dtype);
+  if (st != FA2_OK) return st;
+  // a bound of N or more keys is no bound (this also keeps the kernels'
+  // index arithmetic in range)
+  const int wl = window_left >= N ? -1 : window_left;
+  const int wr = window_right >= N ? -1 : window_right;
+  const bool causal = (wl == -1 && wr == 0);
+  // the fp32 kernel implements no mask and the causal mask only
+  if (in_dtype == FA2_F32 && !(wl == -1 && (wr == -1 || wr == 0))) return FA2_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA2_ERR_INVALID_ARG;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t esz = in_dtype == FA2_BF16 ? 2 : 4;
+  const size_t q_bytes = elems * esz;
+  const size_t kv_bytes = (size_t)B * H_kv * N * d * esz;
+  const size_t o_bytes = elems * (o_dtype == FA2_BF16 ? 2 : 4);
+  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t in_sz[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, o_bytes, ins[i], in_sz[i]) || overlaps(lse, lse_bytes, ins[i], in_sz[i]))
+      return FA2_ERR_INVALID_ARG;
+  }
+  if (overlaps(o, o_bytes, lse, lse_bytes)) return FA2_ERR_INVALID_ARG;
+
+  a->q = q; a->k = k; a->v = v; a->o = o; a->lse = lse;
+  a->B = B; a->H = H; a->N = N; a->d = d;
+  a->Hkv = H_kv;
+  a->causal = causal;
+  a->wl = wl;
+  a->wr = wr;
+  a->scale = scale;
+  a->o_bf16 = (o_dtype == FA2_BF16);
+  const char* dbg = std::getenv("FA2_DEBUG_POISON");
+  a->poison = dbg != nullptr && dbg[0] != '\0' && dbg[0] != '0';
+  a->stream = reinterpret_cast<hipStream_t>(stream);
+  return FA2_OK;
+}
+
+// ---- split schedules ----------------------------------------------------------
+static_assert(sizeof(fa2_split_item) == sizeof(fa2::SplitItem), "fa2_split_item and SplitItem must match");
+static_assert(offsetof(fa2_split_item, n_parts) == offsetof(fa2::SplitItem, n_parts), "layout mismatch");
+
+// Cost model of the bf16 forward kernel in units of one key-tile step of
+// one workgroup: the fixed cost of a workgroup (its Q rows, the first
+// copies, the epilogue), the HBM cost of writing and re-reading one partial
+// result (256 rows x (d fp32 + 2 log-sums), about 0.07 us at 4 TB/s against
+// about 2 us per key-tile step at d = 128; both scale with d), and the
+// merge kernel's launch.
+constexpr double kItemSteps = 2.0;
+constexpr double kPartialSteps = 0.035;
+constexpr double kMergeLaunchSteps = 2.0;
+// split only when the model predicts at least this gain
+constexpr double kSplitMinGain = 0.95;
+constexpr int kMinChunkTiles = 2;
+
+struct KeyRange {
+  int tile, lo, hi;  // key tiles [lo, hi) visible to some row of the tile
+};
+
+// The key tiles the bf16 kernel streams for each query tile under the
+// window (the same band rule as the kernel).
+std::vector<KeyRange> key_ranges(int N, int wl, int wr) {
+  const int br = fa2::kBf16BlockRows, bc = fa2::kBf16BlockCols;
+  const int T = (N + br - 1) / br, nk = (N + bc - 1) / bc;
+  std::vector<KeyRange> out((size_t)T);
+  for (int t = 0; t < T; ++t) {
+    const int q0 = t * br, q_last = std::min(q0 + br, N) - 1;
+    const int lo = wl >= 0 ? std::max(0, q0 - wl) / bc : 0;
+    const int hi = wr >= 0 ? std::min(nk, (q_last + wr) / bc + 1) : nk;
+    out[(size_t)t] = {t, lo, hi};
+  }
+  return out;
+}
+
+// Cut every range of more than `chunk` key tiles (0: none) into equal
+// chunks; list them longest first.  Returns the number of partial slots.
+int make_schedule(const std::vector<KeyRange>& ranges, int chunk, std::vector<fa2_split_item>* out) {
+  out->clear();
+  int slots = 0;
+  for (const KeyRange& r : ranges) {
+    const int n = r.hi - r.lo;
+    const int parts = (chunk > 0 && n > chunk) ? (n + chunk - 1) / chunk : 1;
+    for (int p = 0; p < parts; ++p) {
+      fa2_split_item it;
+      it.tile = r.tile;
+      it.kt_lo = r.lo + (int)((long long)n * p / parts);
+      it.kt_hi = r.lo + (int)((long long)n * (p + 1) / parts);
+      it.slot = parts > 1 ? slots + p : -1;
+      it.slot0 = parts > 1 ? slots : -1;
+      it.n_parts = parts;
+      out->push_back(it);
+    }
+    if (parts > 1) slots += parts;
+  }
+  std::stable_sort(out->begin(), out->end(), [](const fa2_split_item& a, const fa2_split_item& b) {
+    const int na = a.kt_hi - a.kt_lo, nb = b.kt_hi - b.kt_lo;
+    if (na != nb) return na > nb;
+    return a.tile > b.tile;
+  });
+  return slots;
+}
+
+// Predicted duration of a schedule: the workgroups (item-major, B*H per
+// item) go in grid order to whichever unit frees first; plus the partial
+// traffic and the merge.
+double schedule_cost(const std::vector<fa2_split_item>& items, int slots, long long bh, int units) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int u = 0; u < units; ++u) free_at.push(0.0);
+  double end = 0.0;
+  for (const fa2_split_item& it : items) {
+    const double cost = kItemSteps + (it.kt_hi - it.kt_lo);
+    for (long long h = 0; h < bh; ++h) {
+      const double t0 = free_at.top();
+      free_at.pop();
+      free_at.push(t0 + cost);
+      end = std::max(end, t0 + cost);
+    }
+  }
+  if (slots > 0) end += kMergeLaunchSteps + kPartialSteps * (double)slots * (double)bh;
+  return end;
+}
+
+size_t split_workspace_bytes(int B, int H, int d, int slots) {
+  return (size_t)B * H * slots * fa2::kBf16BlockRows * ((size_t)d * sizeof(float) + 2 * sizeof(float));
 }
 
 }  // namespace
@@ -117,52 +257,108 @@ int fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse
 int fa2_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int H_kv, int N, int d, int window_left, int window_right, float scale, void* stream,
                    int in_dtype, int o_dtype) {
-  if (!q || !k || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
-  if (window_left < -1 || window_right < -1) return FA2_ERR_INVALID_ARG;
-  if (H_kv < 1 || H < 1 || H % H_kv != 0) return FA2_ERR_INVALID_ARG;
-  if (!is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
+  fa2::FwdArgs a;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, scale, stream,
+                             in_dtype, o_dtype, &a);
+  if (st != FA2_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+  const hipError_t e = (in_dtype == FA2_BF16) ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+int fa2_split_plan(int B, int H, int N, int d, int window_left, int window_right, int in_dtype,
+                   int num_units, int max_chunk_tiles, fa2_split_item* items, int max_items, int* n_items,
+                   int* n_slots, size_t* workspace_bytes) {
+  if (!n_items || !n_slots || !workspace_bytes) return FA2_ERR_INVALID_ARG;
+  if (window_left < -1 || window_right < -1 || max_chunk_tiles < 0 || max_items < 0) return FA2_ERR_INVALID_ARG;
+  if (max_chunk_tiles == 0 && num_units < 1) return FA2_ERR_INVALID_ARG;
   const int st = check_sizes(B, H, N, d, in_dtype);
   if (st != FA2_OK) return st;
-  // a bound of N or more keys is no bound (this also keeps the kernels'
-  // index arithmetic in range)
+  if (in_dtype != FA2_BF16) return FA2_ERR_UNSUPPORTED;
   const int wl = window_left >= N ? -1 : window_left;
   const int wr = window_right >= N ? -1 : window_right;
-  const bool causal = (wl == -1 && wr == 0);
-  // the fp32 kernel implements no mask and the causal mask only
-  if (in_dtype == FA2_F32 && !(wl == -1 && (wr == -1 || wr == 0))) return FA2_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-    return FA2_ERR_INVALID_ARG;
-  const size_t elems = (size_t)B * H * N * d;
-  const size_t esz = in_dtype == FA2_BF16 ? 2 : 4;
-  const size_t q_bytes = elems * esz;
-  const size_t kv_bytes = (size_t)B * H_kv * N * d * esz;
-  const size_t o_bytes = elems * (o_dtype == FA2_BF16 ? 2 : 4);
-  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
-  const void* ins[3] = {q, k, v};
-  const size_t in_sz[3] = {q_bytes, kv_bytes, kv_bytes};
-  for (int i = 0; i < 3; ++i) {
-    if (overlaps(o, o_bytes, ins[i], in_sz[i]) || overlaps(lse, lse_bytes, ins[i], in_sz[i]))
-      return FA2_ERR_INVALID_ARG;
+  const std::vector<KeyRange> ranges = key_ranges(N, wl, wr);
+  const long long bh = (long long)B * H;
+  std::vector<fa2_split_item> plan;
+  int slots = 0;
+  if (max_chunk_tiles > 0) {
+    slots = make_schedule(ranges, max_chunk_tiles, &plan);
+  } else {
+    // candidates: no split, and chunks of about total / (k * units) key tiles
+    slots = make_schedule(ranges, 0, &plan);
+    const double whole = schedule_cost(plan, slots, bh, num_units);
+    long long total = 0;
+    for (const KeyRange& r : ranges) total += r.hi - r.lo;
+    total *= bh;
+    double best = whole * kSplitMinGain;
+    for (int kk : {1, 2, 3, 4, 6, 8}) {
+      const long long c = std::max<long long>(kMinChunkTiles, (total + (long long)kk * num_units - 1) /
+                                                                  ((long long)kk * num_units));
+      if (c > (1 << 30)) continue;
+      std::vector<fa2_split_item> cand;
+      const int cs = make_schedule(ranges, (int)c, &cand);
+      if (cs == 0) continue;
+      const double cost = schedule_cost(cand, cs, bh, num_units);
+      if (cost < best) {
+        best = cost;
+        plan.swap(cand);
+        slots = cs;
+      }
+    }
   }
-  if (overlaps(o, o_bytes, lse, lse_bytes)) return FA2_ERR_INVALID_ARG;
+  const long long grid = (long long)plan.size() * bh * 4;
+  if (grid > 0x7fffffffLL) return FA2_ERR_INVALID_ARG;
+  if (items != nullptr) {
+    if ((size_t)max_items < plan.size()) return FA2_ERR_INVALID_ARG;
+    std::copy(plan.begin(), plan.end(), items);
+  }
+  *n_items = (int)plan.size();
+  *n_slots = slots;
+  *workspace_bytes = split_workspace_bytes(B, H, d, slots);
+  return FA2_OK;
+}
+
+int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                  int N, int d, int window_left, int window_right, float scale, void* stream, int in_dtype,
+                  int o_dtype, const fa2_split_item* items, int n_items, int n_slots, void* workspace,
+                  size_t workspace_bytes) {
+  fa2::FwdArgs a;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, scale, stream,
+                             in_dtype, o_dtype, &a);
+  if (st != FA2_OK) return st;
+  if (in_dtype != FA2_BF16) return FA2_ERR_UNSUPPORTED;
+  const long long T = (N + (long long)fa2::kBf16BlockRows - 1) / fa2::kBf16BlockRows;
+  const long long nk = (N + (long long)fa2::kBf16BlockCols - 1) / fa2::kBf16BlockCols;
+  if (items == nullptr || !aligned(items, 4) || n_items < 1 || n_items > T * nk) return FA2_ERR_INVALID_ARG;
+  if (n_slots < 0 || n_slots > n_items) return FA2_ERR_INVALID_ARG;
+  if ((long long)n_items * B * H * 4 > 0x7fffffffLL) return FA2_ERR_INVALID_ARG;
+  const size_t need = split_workspace_bytes(B, H, d, n_slots);
+  if (n_slots > 0 && (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < need))
+    return FA2_ERR_INVALID_ARG;
+  // the schedule and the workspace must not overlap each other or any tensor
+  const size_t items_bytes = (size_t)n_items * sizeof(fa2_split_item);
+  const size_t esz = 2;
+  const size_t q_bytes = (size_t)B * H * N * d * esz;
+  const size_t kv_bytes = (size_t)B * H_kv * N * d * esz;
+  const size_t o_bytes = (size_t)B * H * N * d * (o_dtype == FA2_BF16 ? 2 : 4);
+  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
+  const void* bufs[5] = {q, k, v, o, lse};
+  const size_t sizes[5] = {q_bytes, kv_bytes, kv_bytes, o_bytes, lse_bytes};
+  for (int i = 0; i < 5; ++i) {
+    if (i >= 3 && overlaps(items, items_bytes, bufs[i], sizes[i])) return FA2_ERR_INVALID_ARG;
+    if (n_slots > 0 && overlaps(workspace, need, bufs[i], sizes[i])) return FA2_ERR_INVALID_ARG;
+  }
+  if (n_slots > 0 && overlaps(workspace, need, items, items_bytes)) return FA2_ERR_INVALID_ARG;
 
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
-
-  fa2::FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.B = B; a.H = H; a.N = N; a.d = d;
-  a.Hkv = H_kv;
-  a.causal = causal;
-  a.wl = wl;
-  a.wr = wr;
-  a.scale = scale;
-  a.o_bf16 = (o_dtype == FA2_BF16);
-  const char* dbg = std::getenv("FA2_DEBUG_POISON");
-  a.poison = dbg != nullptr && dbg[0] != '\0' && dbg[0] != '0';
-  a.stream = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = (in_dtype == FA2_BF16) ? fa2::launch_fwd_bf16(a) : fa2::launch_fwd_f32(a);
+  a.items = items;
+  a.n_items = n_items;
+  a.part = n_slots > 0 ? workspace : nullptr;
+  a.n_slots = n_slots;
+  hipError_t e = fa2::launch_fwd_bf16(a);
+  if (e == hipSuccess) e = fa2::launch_split_merge(a);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 

@@ -218,7 +218,8 @@ template <int D, bool MASKED, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
-                     int BH, int N, int T, float c, int poison, int group, int wl, int wr) {
+                     int BH, int N, int T, float c, int poison, int group, int wl, int wr,
+                     const SplitItem* __restrict__ items, float* __restrict__ part, int n_slots) {
   using G = Geo<D>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
@@ -235,10 +236,24 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int half = lane >> 5;          // which 4-key sub-rows of each 8-key group
 
   // Grid: workgroup -> (batch*head, query tile).  Causal tiles are issued
-  // heaviest (latest rows) first.
+  // heaviest (latest rows) first.  With a split schedule (items != null)
+  // the workgroup takes chunk blockIdx.x / BH of the schedule instead: a
+  // query tile and a range of its key tiles, whose partial result goes to
+  // partial slot `slot` (or straight to O and LSE when the tile is not
+  // split).  Every field is clamped, so a malformed schedule cannot index
+  // out of range.
   const int bh = blockIdx.x % BH;
-  const int tr = blockIdx.x / BH;
-  const int t = MASKED ? (T - 1 - tr) : tr;
+  int t, ck_lo = 0, ck_hi = 1 << 30, slot = -1;
+  if (items != nullptr) {
+    const SplitItem it = items[blockIdx.x / BH];
+    t = min(max(it.tile, 0), T - 1);
+    ck_lo = max(it.kt_lo, 0);
+    ck_hi = it.kt_hi;
+    slot = it.slot < n_slots ? it.slot : -1;
+  } else {
+    const int tr = blockIdx.x / BH;
+    t = MASKED ? (T - 1 - tr) : tr;
+  }
 
   const long long head = (long long)bh * N * D;
   // grouped key/value heads: `group` consecutive query heads share one
@@ -285,6 +300,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       j_hi = min(nk, (q_last + wr) / kBc + 1);
       jf_hi = min(jf_hi, qw + wr - (kBc - 1) >= 0 ? (qw + wr - (kBc - 1)) / kBc + 1 : 0);
     }
+    n_tiles = j_hi - j_lo;
+  }
+  if (items != nullptr) {
+    // restrict the streamed key tiles to the chunk (at least one tile)
+    const int j_hi = min(j_lo + n_tiles, max(ck_hi, ck_lo + 1));
+    j_lo = min(max(j_lo, ck_lo), j_hi - 1);
     n_tiles = j_hi - j_lo;
   }
   // This row's visible keys, [key_lo, key_hi]: the mask is two compares per
@@ -677,6 +698,29 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const float lt = sum_halves(l);
   const float ltb = sum_halves(lb);
   if (qrow >= N) return;
+  if (slot >= 0) {
+    // Partial result of a chunk: O normalised by the chunk's own rounded sum,
+    // and the chunk's log-sums of the fp32 and of the rounded probabilities
+    // (-inf, and O = 0, for a row that sees no key of the chunk); the merge
+    // weighs the chunks by them (Mishra, "Another use of mergeable
+    // statistics").
+    const float inv = ltb > 0.f ? 1.0f / ltb : 0.f;
+    float* const po = part + (((long long)bh * n_slots + slot) * kBr + (qrow - q0)) * D;
+#pragma unroll
+    for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        *(float4*)(po + 32 * db + 8 * a4 + 4 * half) =
+            make_float4(oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
+                        oacc[db][4 * a4 + 3] * inv);
+    if (half == 0) {
+      float2* const pl = (float2*)(part + (long long)BH * n_slots * kBr * D) +
+                         ((long long)bh * n_slots + slot) * kBr + (qrow - q0);
+      *pl = make_float2(lt > 0.f ? (m * c + log2f(lt)) * 0.69314718055994531f : -INFINITY,
+                        ltb > 0.f ? (m * c + log2f(ltb)) * 0.69314718055994531f : -INFINITY);
+    }
+    return;
+  }
   const float inv = 1.0f / ltb;
   const long long orow = head + (long long)qrow * D;
 #pragma unroll
@@ -701,7 +745,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 template <int D, bool MASKED, bool OUT_BF16>
 hipError_t launch_t(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
-  const long long grid = (long long)T * a.B * a.H;
+  const long long grid = (long long)(a.items ? a.n_items : T) * a.B * a.H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   // c = scale * log2(e), kept >= 1e-30 so that masked (-inf) scores give
   // exactly 0 even for scale == 0; any c that small already makes every
@@ -709,7 +753,8 @@ hipError_t launch_t(const FwdArgs& a) {
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
-                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr);
+                     a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr,
+                     (const SplitItem*)a.items, (float*)a.part, a.n_slots);
   return hipGetLastError();
 }
 
@@ -719,12 +764,103 @@ hipError_t launch_d(const FwdArgs& a) {
   return a.o_bf16 ? launch_t<D, false, true>(a) : launch_t<D, false, false>(a);
 }
 
+
+// ---- merge of a split schedule's partial results -----------------------------
+// A query tile whose key range was cut into chunks has, per chunk a, a
+// partial output O_a (normalised by the chunk's own sum of rounded
+// probabilities) and two log-sums per row: lse_a over the fp32
+// probabilities and lseb_a over the rounded ones.  Exactly as in one pass,
+//   O   = sum_a exp(lseb_a - lseb) O_a,   lseb = log sum_a exp(lseb_a),
+//   LSE = log sum_a exp(lse_a)
+// (Mishra, "Another use of mergeable statistics": the (max, sum) pairs of
+// disjoint key sets combine associatively).  Workgroup: (chunk item, batch
+// * head, quarter of the tile's rows); only the first chunk of a split tile
+// merges, the other items exit at once.  Each row is D/4 lanes of four
+// columns, so a row's partials are read as whole coalesced rows.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeRowsPerGroup = kBr / 4;
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(const SplitItem* __restrict__ items,
+                                                                  const float* __restrict__ part, void* __restrict__ o,
+                                                                  float* __restrict__ lse, int BH, int N, int T,
+                                                                  int n_slots) {
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRowsPerPass = kMergeThreads / kLanesPerRow;
+  const int quarter = blockIdx.x % 4;
+  const int rest = blockIdx.x / 4;
+  const int bh = rest % BH;
+  const SplitItem it = items[rest / BH];
+  if (it.slot < 0 || it.slot >= n_slots || it.slot != it.slot0) return;
+  const int t = min(max(it.tile, 0), T - 1);
+  const int s0 = it.slot0;
+  const int np = min(it.n_parts, n_slots - s0);
+  const int c4 = 4 * (threadIdx.x % kLanesPerRow);
+  const float* const pbase = part + (long long)bh * n_slots * kBr * D;
+  const float2* const lbase = (const float2*)(part + (long long)BH * n_slots * kBr * D) + (long long)bh * n_slots * kBr;
+  for (int r = quarter * kMergeRowsPerGroup + threadIdx.x / kLanesPerRow; r < (quarter + 1) * kMergeRowsPerGroup;
+       r += kRowsPerPass) {
+    const int row = t * kBr + r;
+    if (row >= N) break;
+    float mb = -INFINITY, ml = -INFINITY;
+    for (int a = 0; a < np; ++a) {
+      const float2 x = lbase[(long long)(s0 + a) * kBr + r];
+      ml = fmaxf(ml, x.x);
+      mb = fmaxf(mb, x.y);
+    }
+    float sl = 0.f, sb = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int a = 0; a < np; ++a) {
+      const float2 x = lbase[(long long)(s0 + a) * kBr + r];
+      if (x.x > -INFINITY) sl += expf(x.x - ml);
+      if (x.y > -INFINITY) {
+        const float wgt = expf(x.y - mb);
+        const float4 y = *(const float4*)(pbase + ((long long)(s0 + a) * kBr + r) * D + c4);
+        sb += wgt;
+        acc.x = fmaf(wgt, y.x, acc.x);
+        acc.y = fmaf(wgt, y.y, acc.y);
+        acc.z = fmaf(wgt, y.z, acc.z);
+        acc.w = fmaf(wgt, y.w, acc.w);
+      }
+    }
+    const float inv = sb > 0.f ? 1.0f / sb : 0.f;
+    const long long orow = (long long)bh * N * D + (long long)row * D + c4;
+    if (OUT_BF16) {
+      bf16x4 y = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
+      *(u32x2*)((__bf16*)o + orow) = __builtin_bit_cast(u32x2, y);
+    } else {
+      *(float4*)((float*)o + orow) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (c4 == 0) lse[(long long)bh * N + row] = sl > 0.f ? ml + logf(sl) : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t launch_merge_d(const FwdArgs& a) {
+  const int T = (a.N + kBr - 1) / kBr;
+  const long long grid = 4LL * a.n_items * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  auto kern = a.o_bf16 ? split_merge_kernel<D, true> : split_merge_kernel<D, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kMergeThreads), 0, a.stream, (const SplitItem*)a.items,
+                     (const float*)a.part, a.o, a.lse, a.B * a.H, a.N, T, a.n_slots);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   switch (a.d) {
     case 64: return launch_d<64>(a);
     case 128: return launch_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_split_merge(const FwdArgs& a) {
+  if (a.items == nullptr || a.n_slots <= 0) return hipSuccess;
+  switch (a.d) {
+    case 64: return launch_merge_d<64>(a);
+    case 128: return launch_merge_d<128>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,6 +6,14 @@
 
 namespace fa2 {
 
+// One chunk of a split forward schedule (the layout of fa2_split_item in
+// fa2.h): query tile `tile`, key tiles [kt_lo, kt_hi) of it; `slot` is the
+// partial-result slot (-1: the chunk is the whole tile and writes O and LSE
+// itself); the tile's chunks use slots slot0 .. slot0 + n_parts - 1.
+struct SplitItem {
+  int tile, kt_lo, kt_hi, slot, slot0, n_parts;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -23,6 +31,13 @@ struct FwdArgs {
   // Debug: fill each LDS ring slot with NaN before a tile is copied into it
   // (bf16 kernel; set from the FA2_DEBUG_POISON environment variable).
   bool poison;
+  // Split schedule (bf16 kernel): device array of n_items chunks, or null
+  // for one workgroup per query tile; partial results go to `part`
+  // (n_slots slots per (batch, head)).
+  const void* items = nullptr;
+  int n_items = 0;
+  void* part = nullptr;
+  int n_slots = 0;
   hipStream_t stream;
 };
 
@@ -67,6 +82,10 @@ constexpr int kBwdQRows = kBwdQWaves * 32;  // 256
 constexpr int kBwdQCols = 64;
 constexpr int kBwdKVKeys = 128;
 constexpr int kBwdKVRows = 32;
+
+// Enqueue the merge of split partial results into O and LSE (after the
+// forward kernel, on the same stream).
+hipError_t launch_split_merge(const FwdArgs& a);
 
 // Enqueue the backward kernels (D, dK/dV, dQ) for bf16 inputs.
 hipError_t launch_bwd_bf16(const BwdArgs& a);

@@ -42,6 +42,8 @@
 #ifndef FA2_H
 #define FA2_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -225,6 +227,105 @@ int fa2_bwd_window(const void* q, const void* k, const void* v, const void* o, c
                    const float* lse, float* delta, void* dq, void* dk, void* dv,
                    int B, int H, int H_kv, int N, int d, int window_left, int window_right,
                    float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype);
+
+/*
+ * fa2_split_item -- one chunk of a split forward schedule: the keys of
+ * query tile `tile` (rows 256*tile .. 256*tile + 255) in key tiles
+ * [kt_lo, kt_hi) (64 keys each).
+ *
+ *   slot     partial-result slot the chunk writes, 0 <= slot < n_slots; or
+ *            -1 when the chunk is the tile's whole key range and writes o
+ *            and lse itself.
+ *   slot0    first slot of the tile's chunks (they use slot0 .. slot0 +
+ *            n_parts - 1); the item with slot == slot0 also merges them.
+ *   n_parts  number of chunks of the tile.
+ */
+typedef struct fa2_split_item {
+  int tile;
+  int kt_lo;
+  int kt_hi;
+  int slot;
+  int slot0;
+  int n_parts;
+} fa2_split_item;
+
+/*
+ * fa2_split_plan -- build a forward schedule that cuts the key range of
+ * the heaviest query tiles into chunks, so that a grid with too few query
+ * tiles to fill the chip (few heads, long sequences, causal) still keeps
+ * every compute unit busy.  Host-only; touches no device.
+ *
+ * Each query tile's visible key tiles (the band of fa2_fwd_window) are cut
+ * into chunks of at most C key tiles; chunks are listed longest first (the
+ * order the hardware dispatches them in).  With max_chunk_tiles == 0 the
+ * library picks C, or no split at all, by simulating the dispatch of the
+ * B*H*n_items workgroups on `num_units` compute units (one resident
+ * workgroup each) under a cost model of the kernels: a per-workgroup
+ * start-up cost, one unit per key tile, and the traffic of writing and
+ * merging partial results.  Without a split every item has slot -1 and
+ * n_slots is 0: fa2_fwd_split then computes exactly what fa2_fwd_window
+ * does.
+ *
+ * Source: Mishra, "FlashAttention-2 and -3: From Algebra to GPU
+ * Scheduling", "Another use of mergeable statistics" (the (max, sum)
+ * statistics of disjoint key ranges merge exactly, which lets a long key
+ * range be cut when the grid is too small); Saraf, "FlashAttention 2:
+ * Three Places the Chip Was Still Waiting", section 2.3 (few heads and
+ * long sequences leave units idle when a block covers a whole head).
+ *
+ *   B, H, N, d, in_dtype            as for fa2_fwd (in_dtype FA2_BF16 only,
+ *                                   else FA2_ERR_UNSUPPORTED).
+ *   window_left, window_right       as for fa2_fwd_window.
+ *   num_units        compute units of the device (>= 1; ignored when
+ *                    max_chunk_tiles > 0).
+ *   max_chunk_tiles  0 = the library's choice; > 0 = cut every tile into
+ *                    chunks of at most this many key tiles.
+ *   items, max_items host array receiving the schedule; items may be NULL
+ *                    (then only the counts are returned).  A non-NULL items
+ *                    with max_items < the item count: FA2_ERR_INVALID_ARG.
+ *   n_items, n_slots, workspace_bytes  (host, non-NULL) receive the number
+ *                    of items, of partial slots per (sequence, head), and
+ *                    the workspace size fa2_fwd_split needs (0 if no split).
+ *
+ * Returns FA2_OK or a negative fa2_status.
+ */
+int fa2_split_plan(int B, int H, int N, int d, int window_left, int window_right, int in_dtype,
+                   int num_units, int max_chunk_tiles, fa2_split_item* items, int max_items,
+                   int* n_items, int* n_slots, size_t* workspace_bytes);
+
+/*
+ * fa2_fwd_split -- fa2_fwd_window over a schedule from fa2_split_plan.
+ *
+ * One workgroup per (item, sequence, head) runs the forward kernel over the
+ * item's key tiles only.  A chunk of a split tile writes its partial result
+ * to the workspace: O normalised by its own sum of (rounded) probabilities
+ * and the log of that sum and of the unrounded one, per row; a second
+ * kernel on the same stream then combines the chunks of each split tile,
+ * weighting each by the exponential of its log-sum, into o and lse.  Tiles
+ * that are not split write o and lse directly.
+ *
+ *   items            DEVICE copy of the schedule (n_items entries, as
+ *                    filled by fa2_split_plan for the same B, H, N, d and
+ *                    window; 4-byte aligned); read only.  A schedule for
+ *                    other sizes cannot make the kernels read or write out
+ *                    of bounds (every field is clamped) but gives wrong
+ *                    results.
+ *   n_items, n_slots as returned by fa2_split_plan.
+ *   workspace        device buffer of at least workspace_bytes as returned
+ *                    by fa2_split_plan, 16-byte aligned, overwritten (NULL
+ *                    allowed when n_slots == 0).  Layout: [B*H][n_slots]
+ *                    [256][d] fp32 partial O, then [B*H][n_slots][256] pairs
+ *                    of fp32 log-sums.
+ *   in_dtype         FA2_BF16 only (else FA2_ERR_UNSUPPORTED).
+ * All other arguments as fa2_fwd_window; the buffers must not overlap one
+ * another.  Two kernels are enqueued when n_slots > 0.  Returns FA2_OK
+ * after enqueueing, else a negative fa2_status.
+ */
+int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int H_kv, int N, int d, int window_left, int window_right,
+                  float scale, void* stream, int in_dtype, int o_dtype,
+                  const fa2_split_item* items, int n_items, int n_slots,
+                  void* workspace, size_t workspace_bytes);
 
 /*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,
