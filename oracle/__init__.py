@@ -22,6 +22,10 @@ from .exact_attention import (  # noqa: F401
     visible,
     visible_window,
     probabilities_window,
+    visible_block_sparse,
+    layout_index,
+    attention_head_block_sparse,
+    attention_ref_block_sparse,
 )
 from .attention_grad import (  # noqa: F401
     attention_grad_head,

@@ -65,6 +65,10 @@ __all__ = [
     "attention_head_window",
     "attention_ref_window",
     "probabilities_window",
+    "visible_block_sparse",
+    "layout_index",
+    "attention_head_block_sparse",
+    "attention_ref_block_sparse",
 ]
 
 
@@ -362,3 +366,76 @@ def probabilities_window(q, k, scale: float, window_left: int, window_right: int
     m = s_vis.max(axis=1)
     p = np.exp(np.where(mask, s - m[:, None], -np.inf))
     return p / p.sum(axis=1, keepdims=True)
+
+
+# --- block-sparse masks ----------------------------------------------------------
+
+def visible_block_sparse(row_ids, key_ids, block_mask, block_q: int, block_k: int, causal: bool) -> np.ndarray:
+    """Boolean mask [len(row_ids), len(key_ids)] of a block-sparse pattern:
+    key j is visible to query i iff block_mask[i // block_q, j // block_k]
+    is set, and also j <= i when causal.
+
+    papermap "FlashAttention-2" explainer, Chapter 03 ("The Downstream
+    Story") and Chapter 05 ("The variant family") name block-sparse
+    attention among the variants built on FlashAttention-2's partitioning;
+    a mask given per (query block, key block) pair, the block sizes fixed,
+    is the plain reading of the name.
+    """
+    rows = np.asarray(row_ids)
+    cols = np.asarray(key_ids)
+    bm = np.asarray(block_mask).astype(bool)
+    vis = bm[(rows // block_q)[:, None], (cols // block_k)[None, :]]
+    if causal:
+        vis = vis & (cols[None, :] <= rows[:, None])
+    return vis
+
+
+def layout_index(b: int, h: int, n_batch: int, n_heads: int, n_layouts: int) -> int:
+    """Which block mask (query) head h of sequence b uses: one mask for all
+    (n_layouts = 1), one per head (n_layouts = H) or one per sequence and
+    head (n_layouts = B*H, index b*H + h)."""
+    if n_layouts == 1:
+        return 0
+    if n_layouts == n_heads:
+        return h
+    if n_layouts == n_batch * n_heads:
+        return b * n_heads + h
+    raise ValueError(f"{n_layouts} block masks fit neither 1, H={n_heads} nor B*H={n_batch * n_heads}")
+
+
+def attention_head_block_sparse(q, k, v, scale: float, block_mask, block_q: int, block_k: int, causal: bool):
+    """Exact attention of one head under a block-sparse mask.  A row that
+    sees no key at all has no softmax; it gets O = 0 and LSE = -inf (the
+    empty sum: exp(LSE) = 0).  Returns (O [N, d], LSE [N]) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = q.shape[0]
+    s = scores(q, k, scale)
+    mask = visible_block_sparse(np.arange(n), np.arange(k.shape[0]), block_mask, block_q, block_k, causal)
+    m, l, num = softmax_stats(s, mask, v)
+    o = np.zeros((n, v.shape[1]), dtype=np.float64)
+    lse = np.full(n, -np.inf)
+    seen = l > 0
+    if seen.any():
+        o[seen], lse[seen] = finalize(m[seen], l[seen], num[seen])
+    return o, lse
+
+
+def attention_ref_block_sparse(q, k, v, scale: float, layouts, block_q: int, block_k: int, causal: bool):
+    """Block-sparse attention over [B, H, N, d] (k, v may have fewer heads:
+    grouped heads as in ``attention_ref_gqa``); ``layouts`` is [L, ceil(N /
+    block_q), ceil(N / block_k)] with L chosen as in ``layout_index``.
+    Returns (O, LSE) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    layouts = np.asarray(layouts)
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    o = np.empty(q.shape[:-1] + (v.shape[-1],), dtype=np.float64)
+    lse = np.empty(q.shape[:-1], dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            mask = layouts[layout_index(b, h, B, H, layouts.shape[0])]
+            o[b, h], lse[b, h] = attention_head_block_sparse(q[b, h], k[b, g], v[b, g], scale, mask,
+                                                             block_q, block_k, causal)
+    return o, lse
+

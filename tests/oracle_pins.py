@@ -376,7 +376,104 @@ def pin_window_special_cases():
         _close(lse, lf, 1e-14, f"window ({wl},{wr}) vs full LSE")
 
 
+def _same_with_inf(a, b, tol, what):
+    """Equal -inf entries, the rest within tol."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    ia, ib = np.isneginf(a), np.isneginf(b)
+    assert np.array_equal(ia, ib), f"{what}: -inf at different places"
+    _close(a[~ia], b[~ib], tol, what)
+
+
+def _brute_force_block_sparse(q, k, v, scale, bm, bq, bk, causal):
+    """Block-sparse attention by explicit loops: the keys of row i are the j
+    whose block (i // bq, j // bk) is set (and j <= i when causal); a row
+    with no key gets O = 0 and LSE = -inf."""
+    n, d, dv = len(q), len(q[0]), len(v[0])
+    o = [[0.0] * dv for _ in range(n)]
+    lse = [-math.inf] * n
+    for i in range(n):
+        keys = [j for j in range(len(k)) if bm[i // bq][j // bk] and (not causal or j <= i)]
+        if not keys:
+            continue
+        s = {j: scale * math.fsum(q[i][t] * k[j][t] for t in range(d)) for j in keys}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in keys}
+        den = math.fsum(w.values())
+        for c in range(dv):
+            o[i][c] = math.fsum(w[j] * v[j][c] for j in keys) / den
+        lse[i] = mx + math.log(den)
+    return np.array(o), np.array(lse)
+
+
+def pin_block_sparse_brute_force():
+    """Random block masks (non-square blocks, ragged last blocks, empty rows)
+    on tiny heads: oracle == explicit loops."""
+    rng = _rng(41)
+    for trial in range(12):
+        n = int(rng.integers(1, 10))
+        bq, bk = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        bm = rng.random(size=(-(-n // bq), -(-n // bk))) < 0.5
+        q, k, v = rng.normal(size=(n, 3)), rng.normal(size=(n, 3)), rng.normal(size=(n, 2))
+        for causal in (False, True):
+            eo, el = _brute_force_block_sparse(q.tolist(), k.tolist(), v.tolist(), 0.7, bm.tolist(), bq, bk, causal)
+            o, lse = ref.attention_head_block_sparse(q, k, v, 0.7, bm, bq, bk, causal)
+            _close(o, eo, 1e-12, f"block-sparse O trial {trial} causal={causal}")
+            _same_with_inf(lse, el, 1e-12, f"block-sparse LSE trial {trial} causal={causal}")
+
+
+def pin_block_sparse_special_cases():
+    """An all-ones mask is dense attention; a block-diagonal mask of b-row
+    blocks is dense attention on each b-row chunk on its own; an all-zero
+    mask gives O = 0 and LSE = -inf everywhere."""
+    rng = _rng(42)
+    n, d = 14, 4
+    q, k, v = rng.normal(size=(n, d)), rng.normal(size=(n, d)), rng.normal(size=(n, 3))
+    for causal in (False, True):
+        eo, el = ref.attention_head(q, k, v, 0.5, causal)
+        o, lse = ref.attention_head_block_sparse(q, k, v, 0.5, np.ones((5, 3), dtype=bool), 3, 5, causal)
+        _close(o, eo, 1e-14, f"all-ones mask O causal={causal}")
+        _close(lse, el, 1e-14, f"all-ones mask LSE causal={causal}")
+        b = 4
+        diag = np.eye(-(-n // b), dtype=bool)
+        o, lse = ref.attention_head_block_sparse(q, k, v, 0.5, diag, b, b, causal)
+        for c0 in range(0, n, b):
+            sl = slice(c0, min(n, c0 + b))
+            eo, el = ref.attention_head(q[sl], k[sl], v[sl], 0.5, causal)
+            _close(o[sl], eo, 1e-14, f"block-diagonal O rows {c0}.. causal={causal}")
+            _close(lse[sl], el, 1e-14, f"block-diagonal LSE rows {c0}.. causal={causal}")
+    o, lse = ref.attention_head_block_sparse(q, k, v, 0.5, np.zeros((2, 2), dtype=bool), 7, 7, False)
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+
+
+def pin_block_sparse_layouts():
+    """One mask for all heads, one per head, or one per (sequence, head):
+    each (b, h) uses the mask its index names."""
+    rng = _rng(43)
+    B, H, n = 2, 3, 6
+    q, k, v = rng.normal(size=(B, H, n, 3)), rng.normal(size=(B, H, n, 3)), rng.normal(size=(B, H, n, 2))
+    masks = rng.random(size=(B * H, 3, 2)) < 0.6
+    masks[:, :, 0] = True  # keep every row non-empty
+    for L in (1, H, B * H):
+        o, lse = ref.attention_ref_block_sparse(q, k, v, 0.9, masks[:L], 2, 3, False)
+        for b in range(B):
+            for h in range(H):
+                idx = {1: 0, H: h, B * H: b * H + h}[L]
+                eo, el = _brute_force_block_sparse(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), 0.9,
+                                                   masks[idx].tolist(), 2, 3, False)
+                _close(o[b, h], eo, 1e-12, f"layouts L={L} O ({b},{h})")
+                _close(lse[b, h], el, 1e-12, f"layouts L={L} LSE ({b},{h})")
+    try:
+        ref.attention_ref_block_sparse(q, k, v, 0.9, masks[:4], 2, 3, False)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("4 masks for B=2, H=3 must be rejected")
+
+
 PINS = [
+    pin_block_sparse_brute_force,
+    pin_block_sparse_special_cases,
+    pin_block_sparse_layouts,
     pin_window_brute_force,
     pin_window_special_cases,
     pin_gqa_head_groups,

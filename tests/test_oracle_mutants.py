@@ -19,6 +19,7 @@ _orig_visible = ref.visible
 _orig_stats = ref.softmax_stats
 _orig_finalize = ref.finalize
 _orig_visible_window = ref.visible_window
+_orig_visible_bs = ref.visible_block_sparse
 
 
 def _stats_no_shift(s, mask, v):
@@ -76,6 +77,16 @@ MUTANTS = {
         & (np.ones((len(r), len(c)), dtype=bool) if wr < 0 else np.asarray(c)[None, :] <= np.asarray(r)[:, None] + wr))),
     "window_sides_swapped": ("visible_window", lambda r, c, wl, wr: _orig_visible_window(r, c, wr, wl)),
     "gqa_heads_reversed": ("kv_head_of", lambda h, n_heads, n_kv: n_kv - 1 - h // (n_heads // n_kv)),
+    "block_mask_transposed": ("visible_block_sparse", lambda r, c, bm, bq, bk, causal: (
+        np.asarray(bm).astype(bool)[(np.asarray(c) // bk)[None, :], (np.asarray(r) // bq)[:, None]]
+        & ((np.asarray(c)[None, :] <= np.asarray(r)[:, None]) if causal else True))),
+    "block_sizes_swapped": ("visible_block_sparse", lambda r, c, bm, bq, bk, causal: _orig_visible_bs(
+        r, c, bm, bk, bq, causal) if bq != bk else _orig_visible_bs(r, c, bm, bq, bk, causal)),
+    "block_causal_dropped": ("visible_block_sparse", lambda r, c, bm, bq, bk, causal: _orig_visible_bs(
+        r, c, bm, bq, bk, False)),
+    "block_ragged_rounding_up": ("visible_block_sparse", lambda r, c, bm, bq, bk, causal: _orig_visible_bs(
+        np.minimum(np.asarray(r) + 1, len(r) - 1), c, bm, bq, bk, causal) & (np.asarray(c)[None, :] <= np.asarray(r)[:, None] if causal else True)),
+    "layout_by_batch": ("layout_index", lambda b, h, nb, nh, nl: 0 if nl == 1 else (b if nl == nh else h)),
 }
 
 
