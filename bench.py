@@ -33,6 +33,13 @@ kernel over the chunks, then the merge of the partial results); otherwise
 a step is fa2_fwd_window.  --split off always runs fa2_fwd_window.  Events
 bracket the whole step, so with a split the kernel time includes the merge.
 
+With --block-sparse DENSITY (forward) every head gets its own seeded random
+mask of 128x128 blocks, each set with probability DENSITY and the diagonal
+blocks always set (workloads.make_block_mask, seed = --seed), combined with
+the workload's causal flag; a step is fa2_fwd_sparse over the lists
+fa2_sparse_plan built (outside the timed region), and the credited work
+counts the visible pairs exactly (4*d flop per pair).
+
 With --pass bwd a step is one fa2_bwd call (the D, dK/dV and dQ kernels) on
 the same workload, with dO drawn from the seeded generator and O and LSE
 from one fa2_fwd call made before timing; throughput is credited backward
@@ -181,7 +188,7 @@ def run_bench(args) -> dict:
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  w.B, w.H, hkv, w.N, w.d, wl, wr, w.scale, handle, in_code, o_code)
     schedule = {"split": False}
-    if args.split == "auto" and w.dtype == "bf16":
+    if args.split == "auto" and w.dtype == "bf16" and args.block_sparse is None:
         splan = fa2.split_plan(w.shape, window=(wl, wr), num_units=props.multi_processor_count)
         if splan.splits:
             items = splan.device_items(dev)
@@ -193,6 +200,25 @@ def run_bench(args) -> dict:
                         "workgroups": splan.n_items * w.B * w.H, "longest_chunk_key_tiles": int(lengths.max()),
                         "workspace_bytes": splan.workspace_bytes}
     fwd_call = fa2.fa2_fwd_split if schedule["split"] else fa2.fa2_fwd_window
+    sparse_pairs = None
+    if args.block_sparse is not None:
+        if args.window is not None or w.dtype != "bf16":
+            raise SystemExit("bench.py: --block-sparse takes a bf16 workload and no --window")
+        bs = 128
+        nb = -(-w.N // bs)
+        bmask = workloads.make_block_mask(w.H, nb, nb, args.block_sparse, seed=args.seed)
+        sp = fa2.fa2_sparse_plan(w.N, bs, bs, bmask, w.causal)
+        sp_ptr, sp_ent = sp.device_arrays(dev)
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, hkv,
+                     w.N, w.d, int(w.causal), w.scale, handle, in_code, o_code, w.H, sp_ptr.data_ptr(),
+                     sp_ent.data_ptr() if sp_ent is not None else None, sp.n_entries)
+        fwd_call = fa2.fa2_fwd_sparse
+        sparse_pairs = w.B * sum(workloads.credited_pairs_block_sparse(w.N, bmask[h], bs, bs, w.causal)
+                                 for h in range(w.H))
+        dense_pairs = w.B * w.H * (w.N * (w.N + 1) // 2 if w.causal else w.N * w.N)
+        schedule = {"split": False, "block_sparse": {"block": [bs, bs], "density": args.block_sparse,
+                                                     "layouts": w.H, "key_tile_entries": sp.n_entries,
+                                                     "visible_pair_fraction": round(sparse_pairs / dense_pairs, 4)}}
     torch.cuda.synchronize()
 
     def step():
@@ -218,12 +244,16 @@ def run_bench(args) -> dict:
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     span_ms = starts[0].elapsed_time(ends[-1])
 
-    flops = (workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal) if args.window is None
-             else 4.0 * w.B * w.H * w.d * workloads.credited_pairs(w.N, wl, wr))
+    if sparse_pairs is not None:
+        flops = 4.0 * w.d * sparse_pairs
+    elif args.window is None:
+        flops = workloads.credited_flops(w.B, w.H, w.N, w.d, w.causal)
+    else:
+        flops = 4.0 * w.B * w.H * w.d * workloads.credited_pairs(w.N, wl, wr)
     value = flops * args.steps / wall / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = (traffic_from_profiles(w.name) if hkv == w.H and args.window is None and not schedule["split"]
-               else None)
+    traffic = (traffic_from_profiles(w.name)
+               if hkv == w.H and args.window is None and not schedule["split"] and sparse_pairs is None else None)
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
     # Algorithmic bytes per launch: Q, K, V read once, O and LSE written once.
     esz = 2 if w.dtype == "bf16" else 4
@@ -282,7 +312,7 @@ def run_bench(args) -> dict:
         "kernel_source_sha256_16": kernel_source_hash(),
         "context_not_target": "pages (A100): FA1 25-40% of peak, FA2 50-73% of peak, up to 230 TFLOP/s",
     }
-    if not args.no_cpu_baseline and args.window is None:
+    if not args.no_cpu_baseline and args.window is None and sparse_pairs is None:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, budget_s=args.cpu_budget)
     return result
 
@@ -473,6 +503,8 @@ def main() -> int:
                     help="key/value heads (grouped heads; default: as many as query heads)")
     ap.add_argument("--split", choices=["auto", "off"], default="auto",
                     help="forward: split heavy query tiles' key ranges when the planner predicts a gain")
+    ap.add_argument("--block-sparse", type=float, default=None, metavar="DENSITY",
+                    help="forward: random 128x128 block mask per head with this block density")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--calibrate-copy", action="store_true")

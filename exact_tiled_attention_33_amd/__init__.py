@@ -17,6 +17,9 @@ Raw entry points (same names and argument order as the C ABI):
         -> SplitPlan (host schedule; key ranges of heavy query tiles cut into chunks)
     fa2_fwd_split(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, scale, stream,
         in_dtype, o_dtype, items, n_items, n_slots, workspace, workspace_bytes) -> int
+    fa2_sparse_plan(N, block_q, block_k, block_mask, causal) -> SparsePlan (host key-tile lists)
+    fa2_fwd_sparse(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, in_dtype, o_dtype,
+        n_layouts, tile_ptr, entries, n_entries) -> int
     fa2_strerror(status) -> str
     fa2_version() -> int
 Convenience wrappers over torch device tensors (k and v may have fewer heads
@@ -26,6 +29,7 @@ than q: grouped key/value heads):
         -> (dq, dk, dv)
     split_plan(q_shape, causal=False, window=None, num_units=None, max_chunk_tiles=0) -> SplitPlan
     forward_split(q, k, v, plan, causal=False, scale=None, ...) -> (o, lse)
+    forward_sparse(q, k, v, plan, scale=None, ...) -> (o, lse)   (plan from fa2_sparse_plan)
 """
 
 from __future__ import annotations
@@ -40,6 +44,7 @@ __all__ = [
     "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
     "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "fa2_bwd_window", "forward", "backward",
     "fa2_split_plan", "fa2_fwd_split", "SplitPlan", "split_plan", "forward_split",
+    "fa2_sparse_plan", "fa2_fwd_sparse", "SparsePlan", "forward_sparse",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -53,8 +58,8 @@ FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
-                    "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_strerror",
-                    "fa2_version")
+                    "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_sparse_plan",
+                    "fa2_fwd_sparse", "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -102,6 +107,38 @@ class SplitPlan:
         key = str(device)
         if key not in self._dev:
             self._dev[key] = torch.from_numpy(self.items).to(device)
+        return self._dev[key]
+
+
+class SparsePlan:
+    """Key-tile lists of a block-sparse mask from fa2_sparse_plan.
+
+    ``tile_ptr`` (int32 [n_layouts * T + 1]) and ``entries`` (uint32) are the
+    host arrays; ``N``, ``causal`` and ``n_layouts`` record what they were
+    built for.
+    """
+
+    def __init__(self, tile_ptr, entries, N: int, causal: bool, n_layouts: int):
+        self.tile_ptr = tile_ptr
+        self.entries = entries
+        self.N = int(N)
+        self.causal = bool(causal)
+        self.n_layouts = int(n_layouts)
+        self._dev = {}
+
+    @property
+    def n_entries(self) -> int:
+        return int(self.entries.shape[0])
+
+    def device_arrays(self, device):
+        """(tile_ptr, entries) as int32 device tensors (copied once per device)."""
+        import torch
+
+        key = str(device)
+        if key not in self._dev:
+            ptr = torch.from_numpy(self.tile_ptr).to(device)
+            ent = torch.from_numpy(self.entries.view("int32")).to(device) if self.n_entries else None
+            self._dev[key] = (ptr, ent)
         return self._dev[key]
 
 
@@ -193,6 +230,18 @@ def load():
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
     ]
+    lib.fa2_sparse_plan.restype = ctypes.c_int
+    lib.fa2_sparse_plan.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+    ]
+    lib.fa2_fwd_sparse.restype = ctypes.c_int
+    lib.fa2_fwd_sparse.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+    ]
     lib.fa2_strerror.restype = ctypes.c_char_p
     lib.fa2_strerror.argtypes = [ctypes.c_int]
     lib.fa2_version.restype = ctypes.c_int
@@ -276,6 +325,37 @@ def fa2_fwd_split(q, k, v, o, lse, B, H, H_kv, N, d, window_left, window_right, 
     return int(load().fa2_fwd_split(q, k, v, o, lse, B, H, H_kv, N, d, int(window_left), int(window_right),
                                     float(scale), stream, in_dtype, o_dtype, items, int(n_items), int(n_slots),
                                     workspace, int(workspace_bytes)))
+
+
+def fa2_sparse_plan(N, block_q, block_k, block_mask, causal) -> SparsePlan:
+    """Raw C call (count, then fill) on a host mask [n_layouts, ceil(N/block_q),
+    ceil(N/block_k)] (any array convertible to bool); raises Fa2Error on a bad
+    status."""
+    import numpy as np
+
+    m = np.ascontiguousarray(np.asarray(block_mask).astype(np.uint8))
+    if m.ndim != 3 or m.shape[1] != -(-N // block_q) or m.shape[2] != -(-N // block_k):
+        raise ValueError(f"block_mask must be [L, {-(-N // block_q)}, {-(-N // block_k)}], got {m.shape}")
+    lib = load()
+    n = ctypes.c_int(0)
+    args = (N, block_q, block_k, m.shape[0], m.ctypes.data, int(causal))
+    st = int(lib.fa2_sparse_plan(*args, None, None, 0, ctypes.byref(n)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_sparse_plan")
+    T = -(-N // 256)
+    ptr = np.zeros(m.shape[0] * T + 1, dtype=np.int32)
+    ent = np.zeros(max(1, n.value), dtype=np.uint32)
+    st = int(lib.fa2_sparse_plan(*args, ptr.ctypes.data, ent.ctypes.data, ent.shape[0], ctypes.byref(n)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_sparse_plan")
+    return SparsePlan(ptr, ent[:n.value].copy(), N, causal, m.shape[0])
+
+
+def fa2_fwd_sparse(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, in_dtype, o_dtype, n_layouts,
+                   tile_ptr, entries, n_entries) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_fwd_sparse(q, k, v, o, lse, B, H, H_kv, N, d, int(causal), float(scale), stream,
+                                     in_dtype, o_dtype, int(n_layouts), tile_ptr, entries, int(n_entries)))
 
 
 def fa2_strerror(status: int) -> str:
@@ -455,4 +535,44 @@ def forward_split(q, k, v, plan: SplitPlan, causal: bool = False, scale: float |
                        items.data_ptr(), plan.n_items, plan.n_slots, ws_ptr, ws_bytes)
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_fwd_split")
+    return out, lse
+
+
+def forward_sparse(q, k, v, plan: SparsePlan, scale: float | None = None, o_dtype=None, out=None, lse=None,
+                   stream=None):
+    """Attention forward under a block-sparse mask (fa2_fwd_sparse); returns
+    (o, lse).  ``plan`` comes from ``fa2_sparse_plan`` for the same N; its
+    causal flag applies.  Other arguments as ``forward``."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if plan.N != N:
+        raise ValueError(f"plan was built for N = {plan.N}, not {N}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of o_dtype")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    ptr, ent = plan.device_arrays(q.device)
+    st = fa2_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                        k.shape[1], N, d, plan.causal, scale, handle, _dtype_code(q.dtype), _dtype_code(o_dtype),
+                        plan.n_layouts, ptr.data_ptr(), ent.data_ptr() if ent is not None else None,
+                        plan.n_entries)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_fwd_sparse")
     return out, lse

@@ -362,6 +362,81 @@ int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* l
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
+int fa2_sparse_plan(int N, int block_q, int block_k, int n_layouts, const unsigned char* block_mask, int causal,
+                    int* tile_ptr, unsigned* entries, int max_entries, int* n_entries) {
+  if (!block_mask || !n_entries || N < 1 || n_layouts < 1 || max_entries < 0) return FA2_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  const int br = fa2::kBf16BlockRows, bc = fa2::kBf16BlockCols, slices = fa2::kBf16Waves;
+  const int rows_per_slice = br / slices;  // 32
+  // every wavefront's rows lie in one query block, every key tile in one key block
+  if (block_q < rows_per_slice || block_q % rows_per_slice != 0) return FA2_ERR_UNSUPPORTED;
+  if (block_k < bc || block_k % bc != 0) return FA2_ERR_UNSUPPORTED;
+  const long long T = (N + (long long)br - 1) / br;
+  const long long nk = (N + (long long)bc - 1) / bc;
+  const long long nqb = (N + (long long)block_q - 1) / block_q;
+  const long long nkb = (N + (long long)block_k - 1) / block_k;
+  if (nk >= (1LL << 24) || (long double)n_layouts * T * nk > 2147483647.0L) return FA2_ERR_INVALID_ARG;
+  long long count = 0;
+  for (long long L = 0; L < n_layouts; ++L) {
+    const unsigned char* m = block_mask + L * nqb * nkb;
+    for (long long t = 0; t < T; ++t) {
+      if (tile_ptr && entries) tile_ptr[L * T + t] = (int)count;
+      for (long long j = 0; j < nk; ++j) {
+        unsigned bits = 0;
+        for (int sl = 0; sl < slices; ++sl) {
+          const long long r0 = t * br + (long long)sl * rows_per_slice;
+          if (r0 >= N) break;
+          const long long r_last = std::min<long long>(r0 + rows_per_slice, N) - 1;
+          if (causal && j * bc > r_last) continue;  // the slice's rows see no key of the tile
+          if (m[(r0 / block_q) * nkb + (j * bc) / block_k]) bits |= 1u << sl;
+        }
+        if (bits == 0) continue;
+        if (entries) {
+          if (count >= max_entries) return FA2_ERR_INVALID_ARG;
+          entries[count] = (unsigned)j | (bits << 24);
+        }
+        ++count;
+      }
+    }
+  }
+  if (tile_ptr && entries) tile_ptr[n_layouts * T] = (int)count;
+  *n_entries = (int)count;
+  return FA2_OK;
+}
+
+int fa2_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+                   int d, int causal, float scale, void* stream, int in_dtype, int o_dtype, int n_layouts,
+                   const int* tile_ptr, const unsigned* entries, int n_entries) {
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  fa2::FwdArgs a;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, H_kv, N, d, -1, causal ? 0 : -1, scale, stream, in_dtype,
+                             o_dtype, &a);
+  if (st != FA2_OK) return st;
+  if (in_dtype != FA2_BF16) return FA2_ERR_UNSUPPORTED;
+  if (!(n_layouts == 1 || n_layouts == H || (long long)n_layouts == (long long)B * H)) return FA2_ERR_INVALID_ARG;
+  if (!tile_ptr || !aligned(tile_ptr, 4) || n_entries < 0) return FA2_ERR_INVALID_ARG;
+  if (n_entries > 0 && (!entries || !aligned(entries, 4))) return FA2_ERR_INVALID_ARG;
+  const long long T = (N + (long long)fa2::kBf16BlockRows - 1) / fa2::kBf16BlockRows;
+  const size_t ptr_bytes = ((size_t)n_layouts * T + 1) * sizeof(int);
+  const size_t ent_bytes = (size_t)n_entries * sizeof(unsigned);
+  const size_t o_bytes = (size_t)B * H * N * d * (o_dtype == FA2_BF16 ? 2 : 4);
+  const size_t lse_bytes = (size_t)B * H * N * sizeof(float);
+  if (overlaps(tile_ptr, ptr_bytes, o, o_bytes) || overlaps(tile_ptr, ptr_bytes, lse, lse_bytes))
+    return FA2_ERR_INVALID_ARG;
+  if (n_entries > 0 && (overlaps(entries, ent_bytes, o, o_bytes) || overlaps(entries, ent_bytes, lse, lse_bytes)))
+    return FA2_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+  a.sp_ptr = tile_ptr;
+  // with no entries the kernel never reads the entry array; any valid
+  // pointer will do
+  a.sp_ent = n_entries > 0 ? entries : reinterpret_cast<const unsigned*>(tile_ptr);
+  a.n_layouts = n_layouts;
+  a.n_entries = n_entries;
+  const hipError_t e = fa2::launch_fwd_bf16(a);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d,
             int causal, float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype) {

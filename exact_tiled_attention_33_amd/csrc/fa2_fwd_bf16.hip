@@ -214,12 +214,14 @@ __device__ __forceinline__ T pin(T x) {
 // the correction is what keeps the answer exact.
 constexpr float kTileSumLimit = 2147483648.0f;  // 2^31
 
-template <int D, bool MASKED, bool OUT_BF16>
+template <int D, bool MASKED, bool OUT_BF16, bool SPARSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int T, float c, int poison, int group, int wl, int wr,
-                     const SplitItem* __restrict__ items, float* __restrict__ part, int n_slots) {
+                     const SplitItem* __restrict__ items, float* __restrict__ part, int n_slots,
+                     const int* __restrict__ sp_ptr, const unsigned* __restrict__ sp_ent, int n_layouts,
+                     int n_entries) {
   using G = Geo<D>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
@@ -302,6 +304,19 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     n_tiles = j_hi - j_lo;
   }
+  // Block-sparse: the key tiles come from the tile's list (entry = key tile
+  // | wave-slice bits << 24; bit s set when the rows 32s .. 32s+31 of the
+  // tile see keys of that tile), in the list's order.  Offsets and tile
+  // indices are clamped into range.
+  const int slice = 2 * gw + grp;  // this wavefront's 32-row slice of the tile
+  int e0 = 0;
+  if (SPARSE) {
+    const long long pi = (long long)(bh % n_layouts) * T + t;
+    e0 = min(max(sp_ptr[pi], 0), n_entries);
+    const int e1 = min(max(sp_ptr[pi + 1], e0), n_entries);
+    j_lo = 0;
+    n_tiles = e1 - e0;
+  }
   if (items != nullptr) {
     // restrict the streamed key tiles to the chunk (at least one tile)
     const int j_hi = min(j_lo + n_tiles, max(ck_hi, ck_lo + 1));
@@ -312,6 +327,31 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // score (no per-element branching on which bounds exist).
   const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
   const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
+  // the key tile of step j, and whether this wavefront's rows see it
+  auto tile_of = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return min((int)(sp_ent[e0 + j] & 0xFFFFFFu), nk - 1);
+    else return j_lo + j;
+  };
+  auto wave_sees = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return ((sp_ent[e0 + j] >> (24 + slice)) & 1u) != 0u;
+    else return true;
+  };
+  if (SPARSE && n_tiles == 0) {
+    // no key tile: every row of the tile is empty (O = 0, LSE = -inf)
+    if (qrow < N) {
+      const long long orow = head + (long long)qrow * D;
+#pragma unroll
+      for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int dcol = 32 * db + 8 * a4 + 4 * half;
+          if (OUT_BF16) *(u32x2*)((__bf16*)o + orow + dcol) = u32x2{0u, 0u};
+          else *(float4*)((float*)o + orow + dcol) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      if (half == 0) lse[(long long)bh * N + qrow] = -INFINITY;
+    }
+    return;
+  }
 
   // Tile copies: instruction i of a tile fills LDS slots [64i, 64i + 64);
   // slot u is (row u / slots-per-row, chunk u % slots-per-row), and the
@@ -340,7 +380,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr bool K_TILE = decltype(is_k)::value;
     constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
     constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
-    const int key0 = (j_lo + j) * kBc;
+    const int key0 = tile_of(j) * kBc;
     const int rows = min(kBc, N - key0);
     const unsigned long long gsrc = uniform_addr(src + (long long)key0 * D);
     const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
@@ -501,8 +541,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // banked l and O^T corrected and P recomputed.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   auto vector_phase = [&](int j) __attribute__((always_inline)) {
-    const int ja = j_lo + j;  // key tile index
-    if (ja < jf_lo || ja >= jf_hi) {
+    const int ja = tile_of(j);  // key tile index
+    const bool sees = wave_sees(j);
+    if (!sees || ja < jf_lo || ja >= jf_hi) {
       // a real branch: tiles inside every row's band skip the mask (the
       // empty volatile statement keeps the compiler from applying it to
       // every tile as selects)
@@ -514,7 +555,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          sacc[kb][i] = (key >= key_lo) & (key <= key_hi) ? sacc[kb][i] : -INFINITY;
+          sacc[kb][i] = (key >= key_lo) & (key <= key_hi) & sees ? sacc[kb][i] : -INFINITY;
         }
     }
     sacc[0] = pin(sacc[0]);
@@ -721,7 +762,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     return;
   }
-  const float inv = 1.0f / ltb;
+  // (a row that saw no key -- possible only under a block-sparse mask --
+  // has ltb = 0: O = 0 and LSE = -inf)
+  const float inv = ltb > 0.f ? 1.0f / ltb : 0.f;
   const long long orow = head + (long long)qrow * D;
 #pragma unroll
   for (int db = 0; db < G::kDBlocks; ++db)
@@ -742,7 +785,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (half == 0) lse[(long long)bh * N + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
 }
 
-template <int D, bool MASKED, bool OUT_BF16>
+template <int D, bool MASKED, bool OUT_BF16, bool SPARSE>
 hipError_t launch_t(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)(a.items ? a.n_items : T) * a.B * a.H;
@@ -751,17 +794,24 @@ hipError_t launch_t(const FwdArgs& a) {
   // exactly 0 even for scale == 0; any c that small already makes every
   // probability exactly 1 in fp32.
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16, SPARSE>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
                      a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr,
-                     (const SplitItem*)a.items, (float*)a.part, a.n_slots);
+                     (const SplitItem*)a.items, (float*)a.part, a.n_slots, a.sp_ptr, a.sp_ent,
+                     a.n_layouts, a.n_entries);
   return hipGetLastError();
+}
+
+template <int D, bool SPARSE>
+hipError_t launch_s(const FwdArgs& a) {
+  if (a.wl >= 0 || a.wr >= 0)
+    return a.o_bf16 ? launch_t<D, true, true, SPARSE>(a) : launch_t<D, true, false, SPARSE>(a);
+  return a.o_bf16 ? launch_t<D, false, true, SPARSE>(a) : launch_t<D, false, false, SPARSE>(a);
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a) {
-  if (a.wl >= 0 || a.wr >= 0) return a.o_bf16 ? launch_t<D, true, true>(a) : launch_t<D, true, false>(a);
-  return a.o_bf16 ? launch_t<D, false, true>(a) : launch_t<D, false, false>(a);
+  return a.sp_ptr ? launch_s<D, true>(a) : launch_s<D, false>(a);
 }
 
 

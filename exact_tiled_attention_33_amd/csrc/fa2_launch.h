@@ -38,6 +38,13 @@ struct FwdArgs {
   int n_items = 0;
   void* part = nullptr;
   int n_slots = 0;
+  // Block-sparse list (bf16 kernel): per (layout, query tile) offsets
+  // sp_ptr[n_layouts*T + 1] into the entries sp_ent[n_entries]; layout of
+  // (b, h) = (b*H + h) % n_layouts.  Null: dense.
+  const int* sp_ptr = nullptr;
+  const unsigned* sp_ent = nullptr;
+  int n_layouts = 1;
+  int n_entries = 0;
   hipStream_t stream;
 };
 

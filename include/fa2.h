@@ -328,6 +328,75 @@ int fa2_fwd_split(const void* q, const void* k, const void* v, void* o, float* l
                   void* workspace, size_t workspace_bytes);
 
 /*
+ * fa2_sparse_plan -- turn a block-sparse mask into the per-query-tile key
+ * tile lists fa2_fwd_sparse streams.  Host-only; touches no device.
+ *
+ * Mask: key j is visible to query i iff
+ *     block_mask[L][i / block_q][j / block_k] != 0   (and j <= i if causal),
+ * with L the layout of the (sequence, head) (see fa2_fwd_sparse).  A query
+ * that sees no key has no softmax: fa2_fwd_sparse writes O = 0 and
+ * LSE = -inf for it.
+ *
+ * Source: papermap "FlashAttention-2" explainer, Chapter 03 ("The
+ * Downstream Story") and Chapter 05 ("The variant family"): block-sparse
+ * kernels are named among the variants built on FlashAttention-2's
+ * partitioning; a mask per (query block, key block) pair is the plain
+ * reading.  Key tiles with no visible key are never loaded.
+ *
+ *   N                  sequence length (>= 1).
+ *   block_q, block_k   block sizes: block_q a multiple of 32, block_k a
+ *                      multiple of 64 (else FA2_ERR_UNSUPPORTED), so that
+ *                      each 32-row slice of a query tile lies in one query
+ *                      block and each 64-key tile in one key block.
+ *   n_layouts          number of masks (>= 1).
+ *   block_mask         host bytes [n_layouts][ceil(N/block_q)][ceil(N/block_k)],
+ *                      nonzero = visible block.
+ *   causal             0 or 1: also apply j <= i.
+ *   tile_ptr           host int[n_layouts * ceil(N/256) + 1] receiving, per
+ *                      (layout, 256-row query tile), the offset of its list
+ *                      in `entries` (and the total at the end); may be NULL
+ *                      together with entries (count only).
+ *   entries            host array receiving the lists: key tile index (64
+ *                      keys each) in bits 0-23, and in bit 24 + s whether the
+ *                      query rows 32s .. 32s+31 of the tile see that key
+ *                      tile; ascending key tiles.  NULL: count only.
+ *   max_entries        capacity of entries (FA2_ERR_INVALID_ARG if short).
+ *   n_entries          (host, non-NULL) receives the number of entries.
+ *
+ * Returns FA2_OK or a negative fa2_status.
+ */
+int fa2_sparse_plan(int N, int block_q, int block_k, int n_layouts, const unsigned char* block_mask,
+                    int causal, int* tile_ptr, unsigned* entries, int max_entries, int* n_entries);
+
+/*
+ * fa2_fwd_sparse -- fa2_fwd_gqa under a block-sparse mask, over the lists
+ * fa2_sparse_plan built.
+ *
+ * Each workgroup streams only its query tile's listed key tiles; a
+ * wavefront whose rows do not see a listed tile masks it whole, and the
+ * causal mask (if causal) applies inside tiles as in fa2_fwd.  Rows with no
+ * visible key get O = 0 and LSE = -inf.
+ *
+ *   n_layouts          1 (one mask for every head), H (one per query head,
+ *                      shared by the batch) or B*H (one per (b, h), index
+ *                      b*H + h); else FA2_ERR_INVALID_ARG.  Must match the
+ *                      plan.
+ *   tile_ptr, entries  DEVICE copies of fa2_sparse_plan's outputs for the
+ *                      same N and causal flag (4-byte aligned, read only;
+ *                      entries may be NULL when n_entries == 0).  Offsets
+ *                      and tile indices are clamped into range, so a plan
+ *                      for other sizes cannot make the kernel read or write
+ *                      out of bounds, but gives wrong results.
+ *   in_dtype           FA2_BF16 only (else FA2_ERR_UNSUPPORTED).
+ * All other arguments as fa2_fwd_gqa.  Returns FA2_OK after enqueueing,
+ * else a negative fa2_status.
+ */
+int fa2_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, int causal, float scale,
+                   void* stream, int in_dtype, int o_dtype, int n_layouts,
+                   const int* tile_ptr, const unsigned* entries, int n_entries);
+
+/*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,
  * for reporting and tests.  Host-only; touches no device.
  */

@@ -1,0 +1,122 @@
+"""GPU parity of block-sparse attention (fa2_sparse_plan + fa2_fwd_sparse)
+against the fp64 oracle, every element, at the forward bars (bf16 inputs:
+|O| <= 1e-2, |LSE| <= 1e-3 with fp32 O; a bf16 O may add half an ulp of
+the reference).  Rows that see no key must give exactly O = 0 and
+LSE = -inf, as the oracle does.
+
+Masks are seeded random block patterns with blocks of 32 to 512 rows and
+64 to 256 keys (so some wavefronts of a tile see a listed key tile and
+others do not), causal or not, one mask for all heads, one per head or one
+per (sequence, head), with ragged lengths, d = 64 and 128, grouped
+key/value heads and bf16 O.  An all-ones mask must give bitwise what
+fa2_fwd gives.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_33_amd as fa2
+import oracle.exact_attention as ref
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _bf16_half_ulp(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def _inputs(B, H, H_kv, N, d, seed, outliers=False):
+    w = workloads.get("long_causal").with_(B=B, H=H, N=N, d=d, outlier_frac=0.001 if outliers else 0.0)
+    q, k, v = workloads.make_inputs(w, seed)
+    return q, k[:, :H_kv].contiguous(), v[:, :H_kv].contiguous()
+
+
+CASES = [
+    # B, H, H_kv, N, d, block_q, block_k, layouts ("one", "head", "all"), density, causal, keep_diag, o_bf16
+    (1, 2, 2, 700, 128, 128, 128, "one", 0.4, False, True, False),
+    (1, 2, 2, 700, 128, 128, 128, "head", 0.4, True, True, False),
+    (2, 2, 1, 1000, 128, 64, 192, "all", 0.3, True, False, False),
+    (1, 3, 3, 513, 128, 32, 64, "head", 0.5, False, False, True),
+    (1, 2, 2, 777, 64, 256, 128, "one", 0.5, True, True, False),
+    (1, 1, 1, 2049, 128, 512, 256, "one", 0.3, True, False, False),
+    (2, 4, 2, 300, 64, 96, 64, "all", 0.6, False, False, True),
+    (1, 2, 2, 1024, 128, 128, 64, "head", 0.15, False, False, False),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,bq,bk,lay,dens,causal,diag,o_bf16", CASES,
+                         ids=[f"{b}x{h}/{hk}x{n}x{d}-b{bq}x{bk}-{lay}-p{p}{'-causal' if c else ''}{'-bf16o' if ob else ''}"
+                              for b, h, hk, n, d, bq, bk, lay, p, c, _, ob in CASES])
+def test_sparse_every_element(B, H, H_kv, N, d, bq, bk, lay, dens, causal, diag, o_bf16):
+    q, k, v = _inputs(B, H, H_kv, N, d, seed=1300 + N + bq, outliers=(N % 2 == 1))
+    L = {"one": 1, "head": H, "all": B * H}[lay]
+    bm = workloads.make_block_mask(L, -(-N // bq), -(-N // bk), dens, seed=N + bk, keep_diagonal=diag)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[case] sparse {B}x{H}/{H_kv}x{N}x{d} blocks {bq}x{bk} layouts={L} density={dens} "
+          f"causal={causal}", flush=True)
+    plan = fa2.fa2_sparse_plan(N, bq, bk, bm, causal)
+    o_dtype = torch.bfloat16 if o_bf16 else torch.float32
+    o, lse = fa2.forward_sparse(q.to(DEV), k.to(DEV), v.to(DEV), plan, scale=scale, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    eo, el = ref.attention_ref_block_sparse(_np64(q), _np64(k), _np64(v), scale, bm, bq, bk, causal)
+    o, lse = _np64(o), _np64(lse)
+    empty = np.isneginf(el)
+    print(f"[sparse] empty rows: {int(empty.sum())} of {empty.size}", flush=True)
+    assert np.array_equal(np.isneginf(lse), empty), "-inf LSE rows differ from the oracle's empty rows"
+    assert np.all(o[empty] == 0.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse[~empty]))
+    err_o = np.abs(o - eo)
+    err_l = float(np.max(np.abs(lse[~empty] - el[~empty]))) if (~empty).any() else 0.0
+    print(f"[sparse] max|dO|={float(np.max(err_o)):.3e} max|dLSE|={err_l:.3e}", flush=True)
+    assert np.all(err_o <= 1e-2 + (_bf16_half_ulp(eo) if o_bf16 else 0.0))
+    assert err_l <= 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_mask_is_bitwise_dense(causal):
+    q, k, v = (t.to(DEV) for t in _inputs(1, 3, 3, 900, 128, seed=31, outliers=True))
+    print(f"[case] all-ones block mask vs dense, causal={causal}", flush=True)
+    bm = np.ones((1, -(-900 // 128), -(-900 // 128)), dtype=bool)
+    plan = fa2.fa2_sparse_plan(900, 128, 128, bm, causal)
+    o1, l1 = fa2.forward(q, k, v, causal=causal, scale=0.09)
+    o2, l2 = fa2.forward_sparse(q, k, v, plan, scale=0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_mask_gives_zero_and_minus_inf():
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 2, 600, 128, seed=32))
+    print("[case] all-zero block mask", flush=True)
+    plan = fa2.fa2_sparse_plan(600, 128, 128, np.zeros((1, 5, 5), dtype=bool), True)
+    assert plan.n_entries == 0
+    o = torch.full(q.shape, 7.0, dtype=torch.float32, device=DEV)
+    lse = torch.full(q.shape[:3], 7.0, dtype=torch.float32, device=DEV)
+    fa2.forward_sparse(q, k, v, plan, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0).item() and torch.all(torch.isneginf(lse)).item()
+
+
+def test_sparse_rejections_on_gpu():
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 2, 600, 128, seed=33))
+    plan = fa2.fa2_sparse_plan(600, 128, 128, np.ones((3, 5, 5), dtype=bool), False)  # 3 layouts, 2 heads
+    with pytest.raises(fa2.Fa2Error):
+        fa2.forward_sparse(q, k, v, plan)
+    good = fa2.fa2_sparse_plan(600, 128, 128, np.ones((1, 5, 5), dtype=bool), False)
+    with pytest.raises(fa2.Fa2Error):
+        fa2.forward_sparse(q.float(), k.float(), v.float(), good)
+    with pytest.raises(ValueError):
+        fa2.forward_sparse(q[:, :, :500].contiguous(), k[:, :, :500].contiguous(), v[:, :, :500].contiguous(), good)

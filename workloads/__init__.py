@@ -137,3 +137,36 @@ def credited_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     """Credited attention-forward work: 4*B*H*N^2*d, halved when causal."""
     f = 4.0 * B * H * N * N * d
     return f / 2.0 if causal else f
+
+
+def make_block_mask(n_layouts: int, n_qblocks: int, n_kblocks: int, density: float, seed: int,
+                    keep_diagonal: bool = True):
+    """Seeded random block-sparse pattern, bool [n_layouts, n_qblocks,
+    n_kblocks]: each block set with probability ``density`` (a CPU
+    torch.Generator seeded with ``seed``), plus the diagonal blocks when
+    ``keep_diagonal`` (so that, with square blocks, every query sees a key)."""
+    g = torch.Generator().manual_seed(seed)
+    m = torch.rand((n_layouts, n_qblocks, n_kblocks), generator=g) < density
+    if keep_diagonal:
+        idx = torch.arange(min(n_qblocks, n_kblocks))
+        m[:, idx, idx] = True
+    return m.numpy()
+
+
+def credited_pairs_block_sparse(N: int, block_mask, block_q: int, block_k: int, causal: bool) -> int:
+    """Visible (query, key) pairs of one layout: for every set block, the
+    pairs of its (ragged) row and key ranges, only those with j <= i when
+    causal."""
+    import numpy as np
+
+    bm = np.asarray(block_mask).astype(bool)
+    total = 0
+    for qb, kb in zip(*np.nonzero(bm)):
+        r0, r1 = qb * block_q, min(N, (qb + 1) * block_q)
+        c0, c1 = kb * block_k, min(N, (kb + 1) * block_k)
+        if not causal:
+            total += (r1 - r0) * (c1 - c0)
+            continue
+        i = np.arange(r0, r1)
+        total += int(np.clip(np.minimum(i, c1 - 1) - c0 + 1, 0, None).sum())
+    return int(total)
