@@ -26,6 +26,9 @@ from .exact_attention import (  # noqa: F401
     layout_index,
     attention_head_block_sparse,
     attention_ref_block_sparse,
+    gather_pages,
+    visible_decode,
+    decode_paged_ref,
 )
 from .attention_grad import (  # noqa: F401
     attention_grad_head,

@@ -69,6 +69,9 @@ __all__ = [
     "layout_index",
     "attention_head_block_sparse",
     "attention_ref_block_sparse",
+    "gather_pages",
+    "visible_decode",
+    "decode_paged_ref",
 ]
 
 
@@ -439,3 +442,60 @@ def attention_ref_block_sparse(q, k, v, scale: float, layouts, block_q: int, blo
                                                              block_q, block_k, causal)
     return o, lse
 
+
+
+# --- decoding from a paged key/value cache -----------------------------------------
+
+def gather_pages(cache, block_table_row, context_len: int, kv_head: int) -> np.ndarray:
+    """The first ``context_len`` keys (or values) of one sequence and one
+    key/value head, from a paged cache [n_pages, page_size, H_kv, d]:
+    logical key j lives in physical page block_table_row[j // page_size] at
+    slot j % page_size."""
+    cache = np.asarray(cache)
+    page_size = cache.shape[1]
+    out = np.empty((context_len, cache.shape[3]), dtype=np.float64)
+    for j in range(context_len):
+        out[j] = cache[int(block_table_row[j // page_size]), j % page_size, kv_head]
+    return out
+
+
+def visible_decode(n_new: int, context_len: int) -> np.ndarray:
+    """Boolean mask [n_new, context_len] for the n_new newest tokens of a
+    sequence whose cache holds context_len keys (the new tokens' own keys
+    included, last): new token i sits at position context_len - n_new + i
+    and sees the keys at positions up to its own (the causal mask)."""
+    pos = context_len - n_new + np.arange(n_new)
+    return np.arange(context_len)[None, :] <= pos[:, None]
+
+
+def decode_paged_ref(q, k_cache, v_cache, block_table, context_lens, scale: float):
+    """Attention of the newest n_q tokens of each sequence over its paged
+    cache.  q [B, H, n_q, d] (query heads grouped on the cache's H_kv heads
+    as in ``kv_head_of``), caches [n_pages, page_size, H_kv, d], block_table
+    [B, max_pages], context_lens [B].  A token that sees no key (its position
+    below 0) gets O = 0 and LSE = -inf.  Returns (O [B, H, n_q, d], LSE
+    [B, H, n_q]) in fp64.
+
+    papermap "FlashAttention-2" explainer, Chapter 03 ("The Downstream
+    Story") names paged-KV decoding among the kernels built on
+    FlashAttention-2; the page-table indirection (logical key -> physical
+    page and slot) is the plain reading of a paged cache, and the result is
+    the exact causal attention of the new tokens over the sequence's keys.
+    """
+    q = _f64(q)
+    B, H, n_q, _ = q.shape
+    Hkv = np.asarray(k_cache).shape[2]
+    o = np.zeros(q.shape[:-1] + (np.asarray(v_cache).shape[3],), dtype=np.float64)
+    lse = np.full(q.shape[:-1], -np.inf)
+    for b in range(B):
+        L = int(context_lens[b])
+        mask = visible_decode(n_q, L)
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            kb = gather_pages(k_cache, block_table[b], L, g)
+            vb = gather_pages(v_cache, block_table[b], L, g)
+            m, l, num = softmax_stats(scores(q[b, h], kb, scale), mask, vb)
+            seen = l > 0
+            if seen.any():
+                o[b, h][seen], lse[b, h][seen] = finalize(m[seen], l[seen], num[seen])
+    return o, lse

@@ -470,7 +470,90 @@ def pin_block_sparse_layouts():
         raise AssertionError("4 masks for B=2, H=3 must be rejected")
 
 
+def _paged_cache(rng, kv, page_size, n_pages_total):
+    """Scatter per-sequence contiguous keys kv[b] ([L_b, H_kv, d]) into a
+    paged cache with randomly permuted physical pages; returns (cache, table)."""
+    perm = rng.permutation(n_pages_total)
+    Hkv, d = kv[0].shape[1], kv[0].shape[2]
+    max_pages = max(-(-len(x) // page_size) for x in kv) or 1
+    cache = rng.normal(size=(n_pages_total, page_size, Hkv, d))  # unused slots hold noise
+    table = np.full((len(kv), max_pages), -1, dtype=np.int64)
+    nxt = 0
+    for b, x in enumerate(kv):
+        for p in range(-(-len(x) // page_size)):
+            phys = perm[nxt]
+            nxt += 1
+            table[b, p] = phys
+            chunk = x[p * page_size:(p + 1) * page_size]
+            cache[phys, :len(chunk)] = chunk
+    return cache, table
+
+
+def pin_decode_matches_causal_rows():
+    """Paged decoding of the n_q newest tokens equals the last n_q rows of
+    plain causal attention over the same keys laid out contiguously,
+    whatever the physical page order."""
+    rng = _rng(51)
+    for trial in range(4):
+        B, Hkv, G, d, page = 2, 2, 2, 5, int(rng.integers(2, 5))
+        n_q = int(rng.integers(1, 4))
+        lens = [int(rng.integers(n_q, 17)) for _ in range(B)]
+        ks = [rng.normal(size=(L, Hkv, d)) for L in lens]
+        vs = [rng.normal(size=(L, Hkv, d)) for L in lens]
+        n_pages = sum(-(-L // page) for L in lens) + 3
+        kc, table = _paged_cache(np.random.default_rng(trial), ks, page, n_pages)
+        vc, table_v = _paged_cache(np.random.default_rng(trial), vs, page, n_pages)
+        assert np.array_equal(table, table_v)
+        q = rng.normal(size=(B, Hkv * G, n_q, d))
+        o, lse = ref.decode_paged_ref(q, kc, vc, table, lens, 0.6)
+        for b in range(B):
+            L = lens[b]
+            for h in range(Hkv * G):
+                g = h // G
+                qfull = rng.normal(size=(L, d))
+                qfull[L - n_q:] = q[b, h]
+                eo, el = ref.attention_rows(qfull, ks[b][:, g], vs[b][:, g], 0.6, True, np.arange(L - n_q, L))
+                _close(o[b, h], eo, 1e-12, f"decode O trial {trial} ({b},{h})")
+                _close(lse[b, h], el, 1e-12, f"decode LSE trial {trial} ({b},{h})")
+
+
+def pin_decode_brute_force():
+    """Tiny paged caches by explicit loops and page lookups, including
+    tokens whose position is below 0 (no key: O = 0, LSE = -inf)."""
+    rng = _rng(52)
+    for trial in range(6):
+        B, Hkv, G, d, page = 2, 1 + trial % 2, 2, 3, 2 + trial % 2
+        n_q = 1 + trial % 3
+        lens = [int(rng.integers(0, 9)) for _ in range(B)]
+        n_pages = 12
+        kc = rng.normal(size=(n_pages, page, Hkv, d))
+        vc = rng.normal(size=(n_pages, page, Hkv, 2))
+        table = np.stack([rng.permutation(n_pages)[:6] for _ in range(B)])
+        q = rng.normal(size=(B, Hkv * G, n_q, d))
+        o, lse = ref.decode_paged_ref(q, kc, vc, table, lens, 0.9)
+        for b in range(B):
+            for h in range(Hkv * G):
+                g = h // G
+                for i in range(n_q):
+                    pos = lens[b] - n_q + i
+                    keys = list(range(0, pos + 1)) if pos >= 0 else []
+                    if not keys:
+                        assert np.all(o[b, h, i] == 0.0) and np.isneginf(lse[b, h, i])
+                        continue
+                    kk = {j: kc[table[b][j // page], j % page, g] for j in keys}
+                    vv = {j: vc[table[b][j // page], j % page, g] for j in keys}
+                    s = {j: 0.9 * math.fsum(q[b, h, i, t] * kk[j][t] for t in range(d)) for j in keys}
+                    mx = max(s.values())
+                    w = {j: math.exp(s[j] - mx) for j in keys}
+                    den = math.fsum(w.values())
+                    eo = [math.fsum(w[j] * vv[j][c] for j in keys) / den for c in range(2)]
+                    _close(o[b, h, i], eo, 1e-12, f"decode brute O trial {trial}")
+                    _close(lse[b, h, i], mx + math.log(den), 1e-12, f"decode brute LSE trial {trial}")
+
+
 PINS = [
+    pin_decode_matches_causal_rows,
+    pin_decode_brute_force,
     pin_block_sparse_brute_force,
     pin_block_sparse_special_cases,
     pin_block_sparse_layouts,

@@ -20,6 +20,7 @@ _orig_stats = ref.softmax_stats
 _orig_finalize = ref.finalize
 _orig_visible_window = ref.visible_window
 _orig_visible_bs = ref.visible_block_sparse
+_orig_gather = ref.gather_pages
 
 
 def _stats_no_shift(s, mask, v):
@@ -87,6 +88,14 @@ MUTANTS = {
     "block_ragged_rounding_up": ("visible_block_sparse", lambda r, c, bm, bq, bk, causal: _orig_visible_bs(
         np.minimum(np.asarray(r) + 1, len(r) - 1), c, bm, bq, bk, causal) & (np.asarray(c)[None, :] <= np.asarray(r)[:, None] if causal else True)),
     "layout_by_batch": ("layout_index", lambda b, h, nb, nh, nl: 0 if nl == 1 else (b if nl == nh else h)),
+    "pages_slot_shifted": ("gather_pages", lambda c, row, L, g: np.array(
+        [np.asarray(c)[int(row[j // np.asarray(c).shape[1]]), (j + 1) % np.asarray(c).shape[1], g] for j in range(L)]
+    ).reshape(L, np.asarray(c).shape[3])),
+    "pages_logical_order": ("gather_pages", lambda c, row, L, g: np.asarray(c)[:, :, g].reshape(-1, np.asarray(c).shape[3])[:L]),
+    "pages_head_zero": ("gather_pages", lambda c, row, L, g: _orig_gather(c, row, L, 0)),
+    "decode_causal_from_start": ("visible_decode", lambda n, L: np.arange(L)[None, :] <= np.arange(n)[:, None]),
+    "decode_sees_all_keys": ("visible_decode", lambda n, L: np.ones((n, L), dtype=bool)),
+    "decode_excludes_own_key": ("visible_decode", lambda n, L: np.arange(L)[None, :] < (L - n + np.arange(n))[:, None]),
 }
 
 
