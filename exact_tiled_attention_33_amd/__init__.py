@@ -20,6 +20,11 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_sparse_plan(N, block_q, block_k, block_mask, causal) -> SparsePlan (host key-tile lists)
     fa2_fwd_sparse(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, in_dtype, o_dtype,
         n_layouts, tile_ptr, entries, n_entries) -> int
+    fa2_decode_paged_workspace(B, H, H_kv, n_q, d, max_context, split_keys=0, num_units=0)
+        -> (split_keys, workspace_bytes)
+    fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages,
+        context_lens, max_context, page_size, n_pages, split_keys, workspace, workspace_bytes,
+        stream, in_dtype, o_dtype) -> int
     fa2_strerror(status) -> str
     fa2_version() -> int
 Convenience wrappers over torch device tensors (k and v may have fewer heads
@@ -30,6 +35,7 @@ than q: grouped key/value heads):
     split_plan(q_shape, causal=False, window=None, num_units=None, max_chunk_tiles=0) -> SplitPlan
     forward_split(q, k, v, plan, causal=False, scale=None, ...) -> (o, lse)
     forward_sparse(q, k, v, plan, scale=None, ...) -> (o, lse)   (plan from fa2_sparse_plan)
+    decode_paged(q, k_cache, v_cache, page_table, context_lens, max_context, ...) -> (o, lse)
 """
 
 from __future__ import annotations
@@ -45,6 +51,7 @@ __all__ = [
     "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "fa2_bwd_window", "forward", "backward",
     "fa2_split_plan", "fa2_fwd_split", "SplitPlan", "split_plan", "forward_split",
     "fa2_sparse_plan", "fa2_fwd_sparse", "SparsePlan", "forward_sparse",
+    "fa2_decode_paged_workspace", "fa2_decode_paged", "decode_paged",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -59,7 +66,8 @@ FA2_ERR_LAUNCH = -4
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
                     "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_sparse_plan",
-                    "fa2_fwd_sparse", "fa2_strerror", "fa2_version")
+                    "fa2_fwd_sparse", "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_strerror",
+                    "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -242,6 +250,18 @@ def load():
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
     ]
+    lib.fa2_decode_paged_workspace.restype = ctypes.c_int
+    lib.fa2_decode_paged_workspace.argtypes = [
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_size_t),
+    ]
+    lib.fa2_decode_paged.restype = ctypes.c_int
+    lib.fa2_decode_paged.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+    ]
     lib.fa2_strerror.restype = ctypes.c_char_p
     lib.fa2_strerror.argtypes = [ctypes.c_int]
     lib.fa2_version.restype = ctypes.c_int
@@ -356,6 +376,25 @@ def fa2_fwd_sparse(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, in_
     """Raw C call: pointers and sizes as Python ints; returns the status code."""
     return int(load().fa2_fwd_sparse(q, k, v, o, lse, B, H, H_kv, N, d, int(causal), float(scale), stream,
                                      in_dtype, o_dtype, int(n_layouts), tile_ptr, entries, int(n_entries)))
+
+
+def fa2_decode_paged_workspace(B, H, H_kv, n_q, d, max_context, split_keys=0, num_units=0):
+    """Raw C call; returns (split_keys, workspace_bytes) or raises Fa2Error."""
+    sk, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+    st = int(load().fa2_decode_paged_workspace(B, H, H_kv, n_q, d, max_context, split_keys, num_units,
+                                               ctypes.byref(sk), ctypes.byref(ws)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_decode_paged_workspace")
+    return sk.value, ws.value
+
+
+def fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages, context_lens,
+                     max_context, page_size, n_pages, split_keys, workspace, workspace_bytes, stream, in_dtype,
+                     o_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, float(scale), page_table,
+                                       max_pages, context_lens, max_context, page_size, n_pages, split_keys,
+                                       workspace, int(workspace_bytes), stream, in_dtype, o_dtype))
 
 
 def fa2_strerror(status: int) -> str:
@@ -575,4 +614,57 @@ def forward_sparse(q, k, v, plan: SparsePlan, scale: float | None = None, o_dtyp
                         plan.n_entries)
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_fwd_sparse")
+    return out, lse
+
+
+def decode_paged(q, k_cache, v_cache, page_table, context_lens, max_context: int, scale: float | None = None,
+                 o_dtype=None, split_keys: int = 0, workspace=None, out=None, lse=None, stream=None):
+    """Attention of the newest n_q tokens over a paged cache (fa2_decode_paged);
+    returns (o, lse).
+
+    q [B, H, n_q, d] bf16; k_cache, v_cache [n_pages, page_size, H_kv, d]
+    bf16; page_table int32 [B, max_pages] and context_lens int32 [B] device
+    tensors; ``max_context`` a host bound of context_lens.  ``split_keys`` 0
+    lets the library pick the chunk; ``workspace`` (device uint8) is
+    allocated here when not given.
+    """
+    import torch
+
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError(f"q must be [B, H, n_q, d], caches [n_pages, page_size, H_kv, d]; got {q.shape}, "
+                         f"{k_cache.shape}, {v_cache.shape}")
+    for t in (q, k_cache, v_cache, page_table, context_lens):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous device tensors")
+    if page_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("page_table and context_lens must be int32")
+    B, H, n_q, d = q.shape
+    n_pages, page_size, H_kv, _ = k_cache.shape
+    if page_table.dim() != 2 or page_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("page_table must be [B, max_pages] and context_lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    units = torch.cuda.get_device_properties(q.device).multi_processor_count
+    split_keys, ws_bytes = fa2_decode_paged_workspace(B, H, H_kv, n_q, d, max_context, split_keys, units)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, n_q, d] tensor of o_dtype")
+    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, n_q] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa2_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, H_kv, n_q, d, scale, page_table.data_ptr(), page_table.shape[1],
+                          context_lens.data_ptr(), max_context, page_size, n_pages, split_keys,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(), handle,
+                          _dtype_code(q.dtype), _dtype_code(o_dtype))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_decode_paged")
     return out, lse

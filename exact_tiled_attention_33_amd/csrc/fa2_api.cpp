@@ -437,6 +437,101 @@ int fa2_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* 
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
+int fa2_decode_paged_workspace(int B, int H, int H_kv, int n_q, int d, int max_context, int split_keys,
+                               int num_units, int* split_keys_out, size_t* workspace_bytes) {
+  if (!split_keys_out || !workspace_bytes) return FA2_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || n_q < 1 || max_context < 1) return FA2_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if ((long long)(H / H_kv) * n_q > fa2::kBf16BlockRows) return FA2_ERR_UNSUPPORTED;
+  const int bc = fa2::kBf16BlockCols;
+  if (split_keys < 0 || split_keys % bc != 0) return FA2_ERR_INVALID_ARG;
+  if (split_keys == 0) {
+    // enough chunks for about two workgroups per compute unit, at least
+    // four key tiles per chunk unless the context is shorter
+    if (num_units < 1) return FA2_ERR_INVALID_ARG;
+    const long long groups = (long long)B * H_kv;
+    const long long want = std::max<long long>(1, (2LL * num_units + groups - 1) / groups);
+    long long keys = (max_context + want - 1) / want;
+    keys = (keys + bc - 1) / bc * bc;
+    const long long floor_keys = std::min<long long>(4 * bc, ((long long)max_context + bc - 1) / bc * bc);
+    split_keys = (int)std::max(keys, floor_keys);
+  }
+  const long long chunks = ((long long)max_context + split_keys - 1) / split_keys;
+  const long double bytes = (long double)B * H_kv * chunks * (H / H_kv) * n_q * ((long double)d * 4 + 8);
+  if (bytes > (long double)(1LL << 50) || (long double)chunks * B * H_kv > 2147483647.0L) return FA2_ERR_INVALID_ARG;
+  *split_keys_out = split_keys;
+  *workspace_bytes = (size_t)bytes;
+  return FA2_OK;
+}
+
+int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+                     int H_kv, int n_q, int d, float scale, const int* page_table, int max_pages,
+                     const int* context_lens, int max_context, int page_size, int n_pages, int split_keys,
+                     void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype) {
+  if (!q || !k_cache || !v_cache || !o || !lse || !page_table || !context_lens || !workspace)
+    return FA2_ERR_INVALID_ARG;
+  if (!is_dtype(in_dtype) || !is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
+  if (max_pages < 1 || n_pages < 1 || page_size < 1 || split_keys < 1) return FA2_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
+  int split_out = 0;
+  size_t need = 0;
+  const int st = fa2_decode_paged_workspace(B, H, H_kv, n_q, d, max_context, split_keys, 0, &split_out, &need);
+  if (st != FA2_OK) return st;
+  if (in_dtype != FA2_BF16) return FA2_ERR_UNSUPPORTED;
+  const int bc = fa2::kBf16BlockCols;
+  if (page_size % bc != 0) return FA2_ERR_UNSUPPORTED;  // a key tile must lie in one page
+  if ((long double)n_pages * page_size * H_kv * d > (long double)(1LL << 60)) return FA2_ERR_INVALID_ARG;
+  if ((long double)max_pages * page_size > 2147483647.0L) return FA2_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return FA2_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(workspace, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4))
+    return FA2_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * n_q;
+  const size_t q_bytes = rows * d * 2;
+  const size_t o_bytes = rows * d * (o_dtype == FA2_BF16 ? 2 : 4);
+  const size_t lse_bytes = rows * sizeof(float);
+  const size_t cache_bytes = (size_t)n_pages * page_size * H_kv * d * 2;
+  const size_t table_bytes = (size_t)B * max_pages * sizeof(int);
+  const size_t lens_bytes = (size_t)B * sizeof(int);
+  // written buffers against everything else
+  const void* outs[3] = {o, lse, workspace};
+  const size_t out_sz[3] = {o_bytes, lse_bytes, need};
+  const void* ins[6] = {q, k_cache, v_cache, page_table, context_lens, nullptr};
+  const size_t in_sz[6] = {q_bytes, cache_bytes, cache_bytes, table_bytes, lens_bytes, 0};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA2_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA2_ERR_INVALID_ARG;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+
+  fa2::FwdArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.Hkv = H_kv; a.N = max_context; a.d = d;
+  a.causal = true;
+  a.wl = -1;
+  a.wr = 0;
+  a.scale = scale;
+  a.o_bf16 = (o_dtype == FA2_BF16);
+  const char* dbg = std::getenv("FA2_DEBUG_POISON");
+  a.poison = dbg != nullptr && dbg[0] != '\0' && dbg[0] != '0';
+  a.part = workspace;
+  a.n_slots = (int)(((long long)max_context + split_keys - 1) / split_keys);
+  a.paged.page_table = page_table;
+  a.paged.ctx_lens = context_lens;
+  a.paged.max_pages = max_pages;
+  a.paged.page_size = page_size;
+  a.paged.n_pages = n_pages;
+  a.paged.n_q = n_q;
+  a.paged.chunk_tiles = split_keys / bc;
+  a.paged.kv_heads = H_kv;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = fa2::launch_decode_paged(a);
+  return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d,
             int causal, float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype) {

@@ -214,14 +214,14 @@ __device__ __forceinline__ T pin(T x) {
 // the correction is what keeps the answer exact.
 constexpr float kTileSumLimit = 2147483648.0f;  // 2^31
 
-template <int D, bool MASKED, bool OUT_BF16, bool SPARSE>
+template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int T, float c, int poison, int group, int wl, int wr,
-                     const SplitItem* __restrict__ items, float* __restrict__ part, int n_slots,
+                     const SplitItem* __restrict__ items, float* __restrict__ part, int n_slots, int part_rows,
                      const int* __restrict__ sp_ptr, const unsigned* __restrict__ sp_ent, int n_layouts,
-                     int n_entries) {
+                     int n_entries, PagedArgs pg) {
   using G = Geo<D>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
@@ -244,9 +244,30 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // partial slot `slot` (or straight to O and LSE when the tile is not
   // split).  Every field is clamped, so a malformed schedule cannot index
   // out of range.
+  //
+  // Paged decoding: BH counts (sequence, key/value head) groups; workgroup
+  // (chunk c, group bh) takes the group's n_q newest tokens of its `group`
+  // query heads (rows bh*nq_rows .. +nq_rows of q, o, lse: the heads of a
+  // group are consecutive) against key tiles c*chunk_tiles .. +chunk_tiles
+  // of the sequence's cache, and always writes a partial result (slot c).
   const int bh = blockIdx.x % BH;
   int t, ck_lo = 0, ck_hi = 1 << 30, slot = -1;
-  if (items != nullptr) {
+  int n_keys = N;         // keys this head attends over
+  int nq_rows = N;        // query rows of this head (or group)
+  int kvh = 0;            // paged: key/value head of the group
+  const int* page_row = nullptr;
+  if constexpr (PAGED) {
+    const int b = bh / pg.kv_heads;
+    kvh = bh % pg.kv_heads;
+    n_keys = min(min(max(pg.ctx_lens[b], 0), pg.max_pages * pg.page_size), N);
+    nq_rows = group * pg.n_q;
+    page_row = pg.page_table + (long long)b * pg.max_pages;
+    t = 0;
+    slot = blockIdx.x / BH;
+    ck_lo = slot * pg.chunk_tiles;
+    ck_hi = ck_lo + pg.chunk_tiles;
+    if (ck_lo * kBc >= n_keys) return;  // chunk past this sequence's context (uniform)
+  } else if (items != nullptr) {
     const SplitItem it = items[blockIdx.x / BH];
     t = min(max(it.tile, 0), T - 1);
     ck_lo = max(it.kt_lo, 0);
@@ -257,9 +278,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     t = MASKED ? (T - 1 - tr) : tr;
   }
 
-  const long long head = (long long)bh * N * D;
+  const long long head = (long long)bh * nq_rows * D;
   // grouped key/value heads: `group` consecutive query heads share one
-  const long long kv_head = (long long)(bh / group) * N * D;
+  // (paged: the cache base; the head is part of each tile's address)
+  const long long kv_head = PAGED ? 0 : (long long)(bh / group) * N * D;
   const __bf16* kh = k + kv_head;
   const __bf16* vh = v + kv_head;
 
@@ -274,8 +296,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // Rows past N read as zeros.
   bf16x8 qf[G::kKSteps];
   {
-    const int rows = max(0, min(kRows, N - qw));
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head + (long long)min(qw, N) * D, rows * D * 2);
+    const int rows = max(0, min(kRows, nq_rows - qw));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head + (long long)min(qw, nq_rows) * D, rows * D * 2);
 #pragma unroll
     for (int s = 0; s < G::kKSteps; ++s)
       qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (l32 * D + 16 * s + 8 * half) * 2));
@@ -288,8 +310,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // rows are computed but fully masked.  This wavefront needs no mask on
   // tiles jf_lo .. jf_hi - 1, whose keys (all below N) every one of its rows
   // sees.
-  const int nk = (N + kBc - 1) / kBc;
-  int j_lo = 0, n_tiles = nk, jf_lo = 0, jf_hi = N / kBc;
+  const int nk = (n_keys + kBc - 1) / kBc;
+  int j_lo = 0, n_tiles = nk, jf_lo = 0, jf_hi = n_keys / kBc;
+  // paged: new token i of n_q sits at position n_keys - n_q + i and sees
+  // the keys up to it; every row sees the tiles wholly below n_keys - n_q + 1
+  if (PAGED) jf_hi = max(0, n_keys - pg.n_q + 1) / kBc;
   if (MASKED) {
     const int q_last = min(q0 + kBr, N) - 1;
     const int w_last = min(qw + kRows, N) - 1;
@@ -317,7 +342,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     j_lo = 0;
     n_tiles = e1 - e0;
   }
-  if (items != nullptr) {
+  if (items != nullptr || PAGED) {
     // restrict the streamed key tiles to the chunk (at least one tile)
     const int j_hi = min(j_lo + n_tiles, max(ck_hi, ck_lo + 1));
     j_lo = min(max(j_lo, ck_lo), j_hi - 1);
@@ -326,7 +351,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // This row's visible keys, [key_lo, key_hi]: the mask is two compares per
   // score (no per-element branching on which bounds exist).
   const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
-  const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
+  const int key_hi = PAGED ? n_keys - pg.n_q + qrow % pg.n_q
+                     : (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
   // the key tile of step j, and whether this wavefront's rows see it
   auto tile_of = [&](int j) __attribute__((always_inline)) {
     if constexpr (SPARSE) return min((int)(sp_ent[e0 + j] & 0xFFFFFFu), nk - 1);
@@ -359,6 +385,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // in-range address would do).  Keys past N read as zeros.  Instruction i
   // is issued by wave i % 8; the per-lane source offsets do not depend on
   // the tile and are computed once.
+  // bytes between consecutive keys in global memory (paged cache:
+  // [page, slot, kv head, d], so H_kv rows of d apart)
+  const int row_bytes = PAGED ? pg.kv_heads * G::kRowBytes : G::kRowBytes;
   constexpr int kCopyK = (G::kInstK + kWaves - 1) / kWaves;
   constexpr int kCopyV = (G::kInstV + kWaves - 1) / kWaves;
   int voff_k[kCopyK], voff_v[kCopyV];
@@ -366,13 +395,13 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   for (int k = 0; k < kCopyK; ++k) {
     const int u = (wave + k * kWaves) * 64 + lane;
     const int chunk = u % G::kSlotsK;
-    voff_k[k] = (u / G::kSlotsK) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
+    voff_k[k] = (u / G::kSlotsK) * row_bytes + (chunk < G::kChunks ? chunk : 0) * 16;
   }
 #pragma unroll
   for (int k = 0; k < kCopyV; ++k) {
     const int u = (wave + k * kWaves) * 64 + lane;
     const int chunk = u % G::kSlotsV;
-    voff_v[k] = (u / G::kSlotsV) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
+    voff_v[k] = (u / G::kSlotsV) * row_bytes + (chunk < G::kChunks ? chunk : 0) * 16;
   }
   const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
   const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
@@ -381,8 +410,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
     constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
     const int key0 = tile_of(j) * kBc;
-    const int rows = min(kBc, N - key0);
-    const unsigned long long gsrc = uniform_addr(src + (long long)key0 * D);
+    const int rows = min(kBc, n_keys - key0);
+    long long src_off = (long long)key0 * D;
+    if constexpr (PAGED) {
+      // a tile lies in one page (page_size is a multiple of kBc)
+      const int page = min(max(page_row[key0 / pg.page_size], 0), pg.n_pages - 1);
+      src_off = ((long long)page * pg.page_size + key0 % pg.page_size) * pg.kv_heads * D + (long long)kvh * D;
+    }
+    const unsigned long long gsrc = uniform_addr(src + src_off);
     const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
     if (poison) {
       // Debug: NaN over the 1 KiB blocks this wave's copies are about to
@@ -405,7 +440,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int k = 0; k < kCopy; ++k) {
       if (wave + k * kWaves < kInst) {
         int vo = K_TILE ? voff_k[k] : voff_v[k];
-        if (ragged) vo = min(vo / G::kRowBytes, rows - 1) * G::kRowBytes + vo % G::kRowBytes;
+        if (ragged) vo = min(vo / row_bytes, rows - 1) * row_bytes + vo % row_bytes;
         copy16_to_lds(gsrc, vo, base + k * kWaves * 1024);
       }
     }
@@ -738,7 +773,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // ---- finalise: one division per row, then O and LSE ----------------------
   const float lt = sum_halves(l);
   const float ltb = sum_halves(lb);
-  if (qrow >= N) return;
+  if (qrow >= nq_rows) return;
   if (slot >= 0) {
     // Partial result of a chunk: O normalised by the chunk's own rounded sum,
     // and the chunk's log-sums of the fp32 and of the rounded probabilities
@@ -746,7 +781,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     // weighs the chunks by them (Mishra, "Another use of mergeable
     // statistics").
     const float inv = ltb > 0.f ? 1.0f / ltb : 0.f;
-    float* const po = part + (((long long)bh * n_slots + slot) * kBr + (qrow - q0)) * D;
+    float* const po = part + (((long long)bh * n_slots + slot) * part_rows + (qrow - q0)) * D;
 #pragma unroll
     for (int db = 0; db < G::kDBlocks; ++db)
 #pragma unroll
@@ -755,8 +790,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             make_float4(oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
                         oacc[db][4 * a4 + 3] * inv);
     if (half == 0) {
-      float2* const pl = (float2*)(part + (long long)BH * n_slots * kBr * D) +
-                         ((long long)bh * n_slots + slot) * kBr + (qrow - q0);
+      float2* const pl = (float2*)(part + (long long)BH * n_slots * part_rows * D) +
+                         ((long long)bh * n_slots + slot) * part_rows + (qrow - q0);
       *pl = make_float2(lt > 0.f ? (m * c + log2f(lt)) * 0.69314718055994531f : -INFINITY,
                         ltb > 0.f ? (m * c + log2f(ltb)) * 0.69314718055994531f : -INFINITY);
     }
@@ -782,10 +817,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   // LSE = ln(sum exp(scale*S)) = ln2 * (m*c + log2 l), with the same c the
   // probabilities used.
-  if (half == 0) lse[(long long)bh * N + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
+  if (half == 0) lse[(long long)bh * nq_rows + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
 }
 
-template <int D, bool MASKED, bool OUT_BF16, bool SPARSE>
+template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED = false>
 hipError_t launch_t(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)(a.items ? a.n_items : T) * a.B * a.H;
@@ -794,11 +829,11 @@ hipError_t launch_t(const FwdArgs& a) {
   // exactly 0 even for scale == 0; any c that small already makes every
   // probability exactly 1 in fp32.
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16, SPARSE>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16, SPARSE, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
                      a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr,
-                     (const SplitItem*)a.items, (float*)a.part, a.n_slots, a.sp_ptr, a.sp_ent,
-                     a.n_layouts, a.n_entries);
+                     (const SplitItem*)a.items, (float*)a.part, a.n_slots, kBr, a.sp_ptr, a.sp_ent,
+                     a.n_layouts, a.n_entries, PagedArgs{});
   return hipGetLastError();
 }
 
@@ -885,6 +920,78 @@ __global__ __launch_bounds__(kMergeThreads) void split_merge_kernel(const SplitI
   }
 }
 
+// Merge of paged decoding's chunks: one workgroup per (sequence, key/value
+// head) group; the group's rows, its chunk count from the sequence's
+// context length, the same combination as split_merge_kernel.  A row that
+// saw no key in any chunk (or a sequence with no key) gets O = 0, LSE = -inf.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ part,
+                                                                   void* __restrict__ o, float* __restrict__ lse,
+                                                                   PagedArgs pg, int groups, int nq_rows,
+                                                                   int n_slots, int max_keys) {
+  constexpr int kLanesPerRow = D / 4;
+  constexpr int kRowsPerPass = kMergeThreads / kLanesPerRow;
+  const int bh = blockIdx.x;
+  const int b = bh / pg.kv_heads;
+  const int n_keys = min(min(max(pg.ctx_lens[b], 0), pg.max_pages * pg.page_size), max_keys);
+  const int nk = (n_keys + kBc - 1) / kBc;
+  const int np = min((nk + pg.chunk_tiles - 1) / pg.chunk_tiles, n_slots);
+  const int c4 = 4 * (threadIdx.x % kLanesPerRow);
+  const float* const pbase = part + (long long)bh * n_slots * nq_rows * D;
+  const float2* const lbase = (const float2*)(part + (long long)groups * n_slots * nq_rows * D) +
+                              (long long)bh * n_slots * nq_rows;
+  for (int r = threadIdx.x / kLanesPerRow; r < nq_rows; r += kRowsPerPass) {
+    float mb = -INFINITY, ml = -INFINITY;
+    for (int a = 0; a < np; ++a) {
+      const float2 x = lbase[(long long)a * nq_rows + r];
+      ml = fmaxf(ml, x.x);
+      mb = fmaxf(mb, x.y);
+    }
+    float sl = 0.f, sb = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int a = 0; a < np; ++a) {
+      const float2 x = lbase[(long long)a * nq_rows + r];
+      if (x.x > -INFINITY) sl += expf(x.x - ml);
+      if (x.y > -INFINITY) {
+        const float wgt = expf(x.y - mb);
+        const float4 y = *(const float4*)(pbase + ((long long)a * nq_rows + r) * D + c4);
+        sb += wgt;
+        acc.x = fmaf(wgt, y.x, acc.x);
+        acc.y = fmaf(wgt, y.y, acc.y);
+        acc.z = fmaf(wgt, y.z, acc.z);
+        acc.w = fmaf(wgt, y.w, acc.w);
+      }
+    }
+    const float inv = sb > 0.f ? 1.0f / sb : 0.f;
+    const long long orow = ((long long)bh * nq_rows + r) * D + c4;
+    if (OUT_BF16) {
+      bf16x4 y = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
+      *(u32x2*)((__bf16*)o + orow) = __builtin_bit_cast(u32x2, y);
+    } else {
+      *(float4*)((float*)o + orow) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (c4 == 0) lse[(long long)bh * nq_rows + r] = sl > 0.f ? ml + logf(sl) : -INFINITY;
+  }
+}
+
+template <int D, bool OUT_BF16>
+hipError_t launch_paged_t(const FwdArgs& a) {
+  const int groups = a.B * a.Hkv;
+  const int nq_rows = (a.H / a.Hkv) * a.paged.n_q;
+  const long long grid = (long long)a.n_slots * groups;
+  if (grid > 0x7fffffffLL || grid < 1) return hipErrorInvalidValue;
+  const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, groups, a.N,
+                     1, c, a.poison ? 1 : 0, a.H / a.Hkv, -1, -1, (const SplitItem*)nullptr, (float*)a.part,
+                     a.n_slots, nq_rows, (const int*)nullptr, (const unsigned*)nullptr, 1, 0, a.paged);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D, OUT_BF16>), dim3((unsigned)groups), dim3(kMergeThreads), 0, a.stream,
+                     (const float*)a.part, a.o, a.lse, a.paged, groups, nq_rows, a.n_slots, a.N);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_merge_d(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
@@ -902,6 +1009,14 @@ hipError_t launch_fwd_bf16(const FwdArgs& a) {
   switch (a.d) {
     case 64: return launch_d<64>(a);
     case 128: return launch_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_paged(const FwdArgs& a) {
+  switch (a.d) {
+    case 64: return a.o_bf16 ? launch_paged_t<64, true>(a) : launch_paged_t<64, false>(a);
+    case 128: return a.o_bf16 ? launch_paged_t<128, true>(a) : launch_paged_t<128, false>(a);
     default: return hipErrorInvalidValue;
   }
 }

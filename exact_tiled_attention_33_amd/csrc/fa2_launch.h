@@ -14,6 +14,21 @@ struct SplitItem {
   int tile, kt_lo, kt_hi, slot, slot0, n_parts;
 };
 
+// Paged key/value cache of a decoding call: caches [n_pages][page_size]
+// [kv_heads][d]; logical key j of sequence b is in page
+// page_table[b*max_pages + j/page_size], slot j % page_size.  Each
+// workgroup takes chunk_tiles key tiles of one (sequence, key/value head).
+struct PagedArgs {
+  const int* page_table = nullptr;
+  const int* ctx_lens = nullptr;
+  int max_pages = 0;
+  int page_size = 0;
+  int n_pages = 0;
+  int n_q = 1;
+  int chunk_tiles = 1;
+  int kv_heads = 1;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -45,6 +60,9 @@ struct FwdArgs {
   const unsigned* sp_ent = nullptr;
   int n_layouts = 1;
   int n_entries = 0;
+  // Paged decoding (launch_decode_paged): n_q new tokens per sequence, N =
+  // the largest context; n_slots = chunks per (sequence, key/value head).
+  PagedArgs paged;
   hipStream_t stream;
 };
 
@@ -93,6 +111,9 @@ constexpr int kBwdKVRows = 32;
 // Enqueue the merge of split partial results into O and LSE (after the
 // forward kernel, on the same stream).
 hipError_t launch_split_merge(const FwdArgs& a);
+
+// Enqueue paged decoding: the chunk kernel, then the merge of its partials.
+hipError_t launch_decode_paged(const FwdArgs& a);
 
 // Enqueue the backward kernels (D, dK/dV, dQ) for bf16 inputs.
 hipError_t launch_bwd_bf16(const BwdArgs& a);

@@ -397,6 +397,73 @@ int fa2_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* 
                    const int* tile_ptr, const unsigned* entries, int n_entries);
 
 /*
+ * fa2_decode_paged_workspace -- chunk size and workspace of a
+ * fa2_decode_paged call.  Host-only; touches no device.
+ *
+ *   B, H, H_kv, n_q, d, max_context   as for fa2_decode_paged.
+ *   split_keys      keys per chunk (a multiple of 64), or 0: the library
+ *                   picks the chunk from max_context, B*H_kv and num_units
+ *                   (about two workgroups per unit, at least 256 keys per
+ *                   chunk unless the context is shorter).
+ *   num_units       compute units of the device (used when split_keys == 0).
+ *   split_keys_out, workspace_bytes  (host, non-NULL) receive the chunk
+ *                   size and the workspace fa2_decode_paged needs for it.
+ * Returns FA2_OK, FA2_ERR_INVALID_ARG or FA2_ERR_UNSUPPORTED (d not 64 or
+ * 128, or more than 256 query rows per key/value head: (H/H_kv)*n_q).
+ */
+int fa2_decode_paged_workspace(int B, int H, int H_kv, int n_q, int d, int max_context, int split_keys,
+                               int num_units, int* split_keys_out, size_t* workspace_bytes);
+
+/*
+ * fa2_decode_paged -- attention of the newest n_q tokens of each sequence
+ * over its keys and values in a paged cache.
+ *
+ * Sequence b has context_lens[b] keys (its new tokens' own keys included,
+ * last); logical key j is stored in physical page page_table[b*max_pages +
+ * j/page_size] at slot j % page_size.  New token i (0 <= i < n_q) sits at
+ * position context_lens[b] - n_q + i and sees the keys at positions up to
+ * its own (causal); a token at a negative position sees none and gets
+ * O = 0, LSE = -inf.  Query head h reads key/value head h / (H/H_kv).
+ *
+ * Source: papermap "FlashAttention-2" explainer, Chapter 03 ("The
+ * Downstream Story"): paged-KV decoding is named among the kernels built on
+ * FlashAttention-2; Mishra, "Another use of mergeable statistics": the
+ * statistics of disjoint key ranges merge exactly, so a long context is
+ * cut into chunks processed in parallel and merged.
+ *
+ * Work: one workgroup per (chunk of split_keys keys, sequence, key/value
+ * head) computes the H/H_kv query heads x n_q tokens of the group against
+ * its chunk (K and V read once per group) and writes a partial result to
+ * the workspace; a second kernel merges each group's chunks into o and lse.
+ *
+ *   q          device, [B, H, n_q, d] in_dtype.
+ *   k_cache, v_cache  device, [n_pages, page_size, H_kv, d] in_dtype.
+ *   o          device, [B, H, n_q, d] in o_dtype, fully overwritten.
+ *   lse        device fp32 [B, H, n_q], fully overwritten.
+ *   page_table device int32 [B, max_pages]; entries are clamped into
+ *              [0, n_pages) (a bad entry reads a wrong page, never out of
+ *              bounds).  Entries past a sequence's context are not read.
+ *   context_lens  device int32 [B]; each is clamped into [0, min(max_context,
+ *              max_pages*page_size)].
+ *   max_context   >= 1: an upper bound of context_lens (it sizes the grid).
+ *   page_size  a multiple of 64 (else FA2_ERR_UNSUPPORTED).
+ *   split_keys keys per chunk, a multiple of 64 (from
+ *              fa2_decode_paged_workspace).
+ *   workspace  device, >= fa2_decode_paged_workspace's bytes for the same
+ *              arguments, 16-byte aligned; overwritten.
+ *   in_dtype   FA2_BF16 only (else FA2_ERR_UNSUPPORTED); o_dtype FA2_F32 or
+ *              FA2_BF16.
+ *   (H/H_kv)*n_q <= 256, d 64 or 128 (else FA2_ERR_UNSUPPORTED).
+ * Written buffers must not overlap any other buffer.  Returns FA2_OK after
+ * enqueueing two kernels on `stream`, else a negative fa2_status.
+ */
+int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                     int B, int H, int H_kv, int n_q, int d, float scale,
+                     const int* page_table, int max_pages, const int* context_lens, int max_context,
+                     int page_size, int n_pages, int split_keys,
+                     void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype);
+
+/*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,
  * for reporting and tests.  Host-only; touches no device.
  */

@@ -170,3 +170,25 @@ def credited_pairs_block_sparse(N: int, block_mask, block_q: int, block_k: int, 
         i = np.arange(r0, r1)
         total += int(np.clip(np.minimum(i, c1 - 1) - c0 + 1, 0, None).sum())
     return int(total)
+
+
+def make_paged_cache(context_lens, H_kv: int, d: int, page_size: int, seed: int, spare_pages: int = 3,
+                     device="cpu"):
+    """Seeded paged key/value cache for decoding: caches [n_pages, page_size,
+    H_kv, d] bf16 filled with randn (unused slots too), and an int32 page
+    table [B, max_pages] assigning each sequence's logical pages to randomly
+    permuted physical pages (entries past a sequence's pages are -1).
+    Returns (k_cache, v_cache, page_table)."""
+    g = torch.Generator().manual_seed(seed)
+    need = [-(-int(L) // page_size) for L in context_lens]
+    n_pages = sum(need) + spare_pages
+    max_pages = max(max(need), 1)
+    k = torch.randn((n_pages, page_size, H_kv, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((n_pages, page_size, H_kv, d), generator=g).to(torch.bfloat16)
+    perm = torch.randperm(n_pages, generator=g)
+    table = torch.full((len(context_lens), max_pages), -1, dtype=torch.int32)
+    nxt = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[nxt:nxt + n].to(torch.int32)
+        nxt += n
+    return k.to(device), v.to(device), table.to(device)
