@@ -34,7 +34,7 @@ a step is fa2_fwd_window.  --split off always runs fa2_fwd_window.  Events
 bracket the whole step, so with a split the kernel time includes the merge.
 
 With --block-sparse DENSITY (forward) every head gets its own seeded random
-mask of 128x128 blocks, each set with probability DENSITY and the diagonal
+mask of 128x128 blocks (--sparse-block ROWS KEYS to change), each set with probability DENSITY and the diagonal
 blocks always set (workloads.make_block_mask, seed = --seed), combined with
 the workload's causal flag; a step is fa2_fwd_sparse over the lists
 fa2_sparse_plan built (outside the timed region), and the credited work
@@ -45,6 +45,14 @@ the same workload, with dO drawn from the seeded generator and O and LSE
 from one fa2_fwd call made before timing; throughput is credited backward
 work (10*B*H*N^2*d, halved when causal) and the CPU baseline times the fp64
 gradient oracle.
+
+With --pass decode a step is one fa2_decode_paged call on a synthetic
+serving batch (DECODE_CONFIG: B sequences whose context lengths are drawn
+uniformly from [L_min, L_max] by a seeded generator, one new token each,
+H query heads on H_kv key/value heads, d = 128, pages of 64 keys in a
+randomly permuted cache).  Decoding is bound by HBM: the line reports GB/s
+of algorithmic traffic (each sequence's keys and values read once, Q read,
+O and LSE written) against the 8 TB/s peak.
 
 Extra modes used to produce committed profile summaries:
     --calibrate-copy      time a plain 1 GiB device copy (counter calibration)
@@ -81,6 +89,8 @@ KERNEL_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_fwd_bf16.hip",
                   "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
                   "exact_tiled_attention_33_amd/csrc/fa2_launch.h"]
 CALIB_BYTES = 1 << 30
+METRIC_DECODE = "paged-KV decode, GB/s of key/value traffic vs MI355X HBM peak"
+DECODE_CONFIG = {"B": 64, "H": 32, "H_kv": 8, "d": 128, "n_q": 1, "page_size": 64, "L_min": 1024, "L_max": 8192}
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -204,19 +214,18 @@ def run_bench(args) -> dict:
     if args.block_sparse is not None:
         if args.window is not None or w.dtype != "bf16":
             raise SystemExit("bench.py: --block-sparse takes a bf16 workload and no --window")
-        bs = 128
-        nb = -(-w.N // bs)
-        bmask = workloads.make_block_mask(w.H, nb, nb, args.block_sparse, seed=args.seed)
-        sp = fa2.fa2_sparse_plan(w.N, bs, bs, bmask, w.causal)
+        bq, bk = args.sparse_block
+        bmask = workloads.make_block_mask(w.H, -(-w.N // bq), -(-w.N // bk), args.block_sparse, seed=args.seed)
+        sp = fa2.fa2_sparse_plan(w.N, bq, bk, bmask, w.causal)
         sp_ptr, sp_ent = sp.device_arrays(dev)
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, hkv,
                      w.N, w.d, int(w.causal), w.scale, handle, in_code, o_code, w.H, sp_ptr.data_ptr(),
                      sp_ent.data_ptr() if sp_ent is not None else None, sp.n_entries)
         fwd_call = fa2.fa2_fwd_sparse
-        sparse_pairs = w.B * sum(workloads.credited_pairs_block_sparse(w.N, bmask[h], bs, bs, w.causal)
+        sparse_pairs = w.B * sum(workloads.credited_pairs_block_sparse(w.N, bmask[h], bq, bk, w.causal)
                                  for h in range(w.H))
         dense_pairs = w.B * w.H * (w.N * (w.N + 1) // 2 if w.causal else w.N * w.N)
-        schedule = {"split": False, "block_sparse": {"block": [bs, bs], "density": args.block_sparse,
+        schedule = {"split": False, "block_sparse": {"block": [bq, bk], "density": args.block_sparse,
                                                      "layouts": w.H, "key_tile_entries": sp.n_entries,
                                                      "visible_pair_fraction": round(sparse_pairs / dense_pairs, 4)}}
     torch.cuda.synchronize()
@@ -452,6 +461,80 @@ def run_bench_bwd(args) -> dict:
     return result
 
 
+def run_bench_decode(args) -> dict:
+    import torch
+
+    import exact_tiled_attention_33_amd as fa2
+    import workloads
+
+    cfg = dict(DECODE_CONFIG)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    g = torch.Generator().manual_seed(args.seed)
+    lens = torch.randint(cfg["L_min"], cfg["L_max"] + 1, (cfg["B"],), generator=g).tolist()
+    kc, vc, table = workloads.make_paged_cache(lens, cfg["H_kv"], cfg["d"], cfg["page_size"], seed=args.seed + 1,
+                                               device=dev)
+    q = torch.randn((cfg["B"], cfg["H"], cfg["n_q"], cfg["d"]), generator=g).to(torch.bfloat16).to(dev)
+    ctx = torch.tensor(lens, dtype=torch.int32, device=dev)
+    max_ctx = max(lens)
+    split, ws_bytes = fa2.fa2_decode_paged_workspace(cfg["B"], cfg["H"], cfg["H_kv"], cfg["n_q"], cfg["d"], max_ctx,
+                                                     args.split_keys, props.multi_processor_count)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o_dtype = torch.bfloat16 if args.o_dtype == "bf16" else torch.float32
+    o = torch.empty(q.shape, dtype=o_dtype, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    call_args = (q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(), cfg["B"], cfg["H"],
+                 cfg["H_kv"], cfg["n_q"], cfg["d"], 1.0 / math.sqrt(cfg["d"]), table.data_ptr(), table.shape[1],
+                 ctx.data_ptr(), max_ctx, cfg["page_size"], kc.shape[0], split, ws.data_ptr(), ws_bytes,
+                 stream.cuda_stream, fa2.BF16, fa2.BF16 if args.o_dtype == "bf16" else fa2.F32)
+    torch.cuda.synchronize()
+
+    def step():
+        st = fa2.fa2_decode_paged(*call_args)
+        if st != fa2.FA2_OK:
+            raise fa2.Fa2Error(st, "fa2_decode_paged")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    avg_ms = sum(per_launch_ms) / len(per_launch_ms)
+    kv_bytes = 2 * sum(lens) * cfg["H_kv"] * cfg["d"] * 2
+    rows = cfg["B"] * cfg["H"] * cfg["n_q"]
+    alg_bytes = kv_bytes + rows * cfg["d"] * 2 + rows * cfg["d"] * (2 if args.o_dtype == "bf16" else 4) + rows * 4
+    flops = 4.0 * cfg["H"] * cfg["d"] * sum(lens) * cfg["n_q"]
+    gbs = alg_bytes / (avg_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC_DECODE,
+        "value": round(alg_bytes * args.steps / wall / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "paged_decode", **cfg, "context_lens_sum": sum(lens), "max_context": max_ctx,
+                   "split_keys": split, "o_dtype": args.o_dtype, "seed": args.seed, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel_ms_avg": round(avg_ms, 4),
+                     "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops,
+                     "arithmetic_intensity": round(flops / alg_bytes, 2)},
+        "timing": {"per_launch_ms_min": round(min(per_launch_ms), 4),
+                   "per_launch_ms_max": round(max(per_launch_ms), 4)},
+        "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+
+
 def calibrate_copy(args) -> None:
     """A plain device-to-device copy of CALIB_BYTES, repeated: its counter
     readings calibrate FETCH_SIZE / WRITE_SIZE against known bytes."""
@@ -494,8 +577,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="workload name (default: the headline one)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--o-dtype", choices=["fp32", "bf16"], default="fp32")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
-                    help="fwd (default): the forward pass; bwd: the backward pass")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode"], default="fwd",
+                    help="fwd (default): the forward pass; bwd: the backward pass; decode: paged-KV decoding")
     ap.add_argument("--window", type=int, nargs=2, default=None, metavar=("LEFT", "RIGHT"),
                     help="sliding-window mask: key j visible to query i iff i-LEFT <= j <= i+RIGHT "
                          "(-1 = unbounded side); overrides the workload's causal flag")
@@ -505,6 +588,10 @@ def main() -> int:
                     help="forward: split heavy query tiles' key ranges when the planner predicts a gain")
     ap.add_argument("--block-sparse", type=float, default=None, metavar="DENSITY",
                     help="forward: random 128x128 block mask per head with this block density")
+    ap.add_argument("--sparse-block", type=int, nargs=2, default=[128, 128], metavar=("ROWS", "KEYS"),
+                    help="block size of the --block-sparse mask (rows a multiple of 32, keys of 64)")
+    ap.add_argument("--split-keys", type=int, default=0,
+                    help="decode: keys per chunk (a multiple of 64; 0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -527,7 +614,10 @@ def main() -> int:
 
     if args.workload is None:
         args.workload = workloads.HEADLINE
-    result = run_bench_bwd(args) if args.which == "bwd" else run_bench(args)
+    if args.which == "decode":
+        result = run_bench_decode(args)
+    else:
+        result = run_bench_bwd(args) if args.which == "bwd" else run_bench(args)
     print(json.dumps(result))
     return 0
 

@@ -446,11 +446,13 @@ int fa2_decode_paged_workspace(int B, int H, int H_kv, int n_q, int d, int max_c
   const int bc = fa2::kBf16BlockCols;
   if (split_keys < 0 || split_keys % bc != 0) return FA2_ERR_INVALID_ARG;
   if (split_keys == 0) {
-    // enough chunks for about two workgroups per compute unit, at least
-    // four key tiles per chunk unless the context is shorter
+    // enough chunks for about eight workgroups per compute unit at the
+    // longest context (shorter sequences have fewer, so about four on
+    // average for a mixed batch), at least four key tiles per chunk unless
+    // the context is shorter
     if (num_units < 1) return FA2_ERR_INVALID_ARG;
     const long long groups = (long long)B * H_kv;
-    const long long want = std::max<long long>(1, (2LL * num_units + groups - 1) / groups);
+    const long long want = std::max<long long>(1, (8LL * num_units + groups - 1) / groups);
     long long keys = (max_context + want - 1) / want;
     keys = (keys + bc - 1) / bc * bc;
     const long long floor_keys = std::min<long long>(4 * bc, ((long long)max_context + bc - 1) / bc * bc);

@@ -8,8 +8,8 @@ import exact_tiled_attention_33_amd as fa2
 
 
 def test_workspace_helper():
-    # 256 groups on 256 units: two chunks of 4096 keys for an 8192-key context
-    assert fa2.fa2_decode_paged_workspace(32, 32, 8, 1, 128, 8192, 0, 256) == (4096, 32 * 8 * 2 * 4 * 1 * (128 * 4 + 8))
+    # 256 groups on 256 units: eight chunks of 1024 keys for an 8192-key context
+    assert fa2.fa2_decode_paged_workspace(32, 32, 8, 1, 128, 8192, 0, 256) == (1024, 32 * 8 * 8 * 4 * 1 * (128 * 4 + 8))
     # a short context: one chunk covering it
     sk, ws = fa2.fa2_decode_paged_workspace(1, 8, 1, 1, 128, 100, 0, 256)
     assert sk == 128 and ws == 1 * 1 * 1 * 8 * (128 * 4 + 8)
