@@ -37,3 +37,4 @@ from .attention_grad import (  # noqa: F401
     delta_rows,
     grad_magnitudes_head,
 )
+from . import fp8_attention  # noqa: F401
