@@ -25,6 +25,9 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages,
         context_lens, max_context, page_size, n_pages, split_keys, workspace, workspace_bytes,
         stream, in_dtype, o_dtype) -> int
+    fa2_fp8_pack_workspace(B, H, N) -> bytes
+    fa2_fp8_pack(x, B, H, N, d, signs, codes, scales, workspace, workspace_bytes, stream) -> int
+    fa2_fwd_fp8(q8, q_scale, k8, k_scale, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, o_dtype) -> int
     fa2_strerror(status) -> str
     fa2_version() -> int
 Convenience wrappers over torch device tensors (k and v may have fewer heads
@@ -36,6 +39,7 @@ than q: grouped key/value heads):
     forward_split(q, k, v, plan, causal=False, scale=None, ...) -> (o, lse)
     forward_sparse(q, k, v, plan, scale=None, ...) -> (o, lse)   (plan from fa2_sparse_plan)
     decode_paged(q, k_cache, v_cache, page_table, context_lens, max_context, ...) -> (o, lse)
+    fp8_pack(x, signs=None) -> (codes, scales);  forward_fp8(q, k, v, signs, ...) -> (o, lse)
 """
 
 from __future__ import annotations
@@ -52,6 +56,7 @@ __all__ = [
     "fa2_split_plan", "fa2_fwd_split", "SplitPlan", "split_plan", "forward_split",
     "fa2_sparse_plan", "fa2_fwd_sparse", "SparsePlan", "forward_sparse",
     "fa2_decode_paged_workspace", "fa2_decode_paged", "decode_paged",
+    "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fp8_pack", "forward_fp8",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -66,8 +71,8 @@ FA2_ERR_LAUNCH = -4
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
                     "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_sparse_plan",
-                    "fa2_fwd_sparse", "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_strerror",
-                    "fa2_version")
+                    "fa2_fwd_sparse", "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_fp8_pack_workspace",
+                    "fa2_fp8_pack", "fa2_fwd_fp8", "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -262,6 +267,19 @@ def load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_fp8_pack_workspace.restype = ctypes.c_int
+    lib.fa2_fp8_pack_workspace.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa2_fp8_pack.restype = ctypes.c_int
+    lib.fa2_fp8_pack.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+    ]
+    lib.fa2_fwd_fp8.restype = ctypes.c_int
+    lib.fa2_fwd_fp8.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+    ]
     lib.fa2_strerror.restype = ctypes.c_char_p
     lib.fa2_strerror.argtypes = [ctypes.c_int]
     lib.fa2_version.restype = ctypes.c_int
@@ -395,6 +413,35 @@ def fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, pag
     return int(load().fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, float(scale), page_table,
                                        max_pages, context_lens, max_context, page_size, n_pages, split_keys,
                                        workspace, int(workspace_bytes), stream, in_dtype, o_dtype))
+
+
+def fa2_fp8_pack_workspace(B, H, N) -> int:
+    """Raw C call; returns the workspace bytes or raises Fa2Error."""
+    ws = ctypes.c_size_t(0)
+    st = int(load().fa2_fp8_pack_workspace(B, H, N, ctypes.byref(ws)))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_fp8_pack_workspace")
+    return ws.value
+
+
+def fa2_fp8_pack(x, B, H, N, d, signs, codes, scales, workspace, workspace_bytes, stream) -> int:
+    """Raw C call: device pointers as ints; ``signs`` a host float32 array
+    of d entries (+-1) or None."""
+    import numpy as np
+
+    sg = None
+    if signs is not None:
+        sg = np.ascontiguousarray(np.asarray(signs, dtype=np.float32))
+        if sg.shape != (d,):
+            raise ValueError(f"signs must have {d} entries")
+    return int(load().fa2_fp8_pack(x, B, H, N, d, sg.ctypes.data if sg is not None else None, codes, scales,
+                                   workspace, int(workspace_bytes), stream))
+
+
+def fa2_fwd_fp8(q8, q_scale, k8, k_scale, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, o_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_fwd_fp8(q8, q_scale, k8, k_scale, v, o, lse, B, H, H_kv, N, d, int(causal),
+                                  float(scale), stream, o_dtype))
 
 
 def fa2_strerror(status: int) -> str:
@@ -667,4 +714,61 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, max_context: int
                           _dtype_code(q.dtype), _dtype_code(o_dtype))
     if st != FA2_OK:
         raise Fa2Error(st, "fa2_decode_paged")
+    return out, lse
+
+
+def fp8_pack(x, signs=None, stream=None, workspace=None):
+    """fa2_fp8_pack on a contiguous bf16 device tensor [B, H, N, d]; returns
+    (codes uint8 [B, H, N, d], scales float32 [B, H]).  ``signs``: d values
+    of +-1 (the rotation), or None for no rotation."""
+    import torch
+
+    if x.dim() != 4 or x.dtype != torch.bfloat16 or not (x.is_cuda and x.is_contiguous()):
+        raise ValueError("x must be a contiguous bf16 device tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    ws_bytes = fa2_fp8_pack_workspace(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    sg = None if signs is None else [float(t) for t in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+    st = fa2_fp8_pack(x.data_ptr(), B, H, N, d, sg, codes.data_ptr(), scales.data_ptr(), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), handle)
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_fp8_pack")
+    return codes, scales
+
+
+def forward_fp8(q, k, v, signs=None, causal: bool = False, scale: float | None = None, o_dtype=None, out=None,
+                lse=None, stream=None, packed=None):
+    """FP8 attention forward: pack Q and K (fp8_pack with the same signs),
+    then fa2_fwd_fp8; returns (o, lse).  q, k, v bf16 device tensors as for
+    ``forward``.  ``packed`` = (q8, q_scale, k8, k_scale) skips the packing."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if packed is None:
+        q8, qs = fp8_pack(q, signs, stream)
+        k8, ks = fp8_pack(k, signs, stream)
+    else:
+        q8, qs, k8, ks = packed
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa2_fwd_fp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v.data_ptr(), out.data_ptr(),
+                     lse.data_ptr(), B, H, k.shape[1], N, d, causal, scale, handle, _dtype_code(o_dtype))
+    if st != FA2_OK:
+        raise Fa2Error(st, "fa2_fwd_fp8")
     return out, lse

@@ -534,6 +534,85 @@ int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, vo
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
+int fa2_fp8_pack_workspace(int B, int H, int N, size_t* workspace_bytes) {
+  if (!workspace_bytes || B < 1 || H < 1 || N < 1) return FA2_ERR_INVALID_ARG;
+  if ((long double)B * H * N > (long double)(1LL << 40)) return FA2_ERR_INVALID_ARG;
+  *workspace_bytes = (size_t)B * H * fa2::fp8_pack_chunks(N) * sizeof(float);
+  return FA2_OK;
+}
+
+int fa2_fp8_pack(const void* x, int B, int H, int N, int d, const float* signs, void* codes, float* scales,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !codes || !scales || !workspace) return FA2_ERR_INVALID_ARG;
+  size_t need = 0;
+  if (fa2_fp8_pack_workspace(B, H, N, &need) != FA2_OK) return FA2_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if (workspace_bytes < need) return FA2_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(workspace, 4))
+    return FA2_ERR_INVALID_ARG;
+  fa2::Fp8Signs sg = {{0u, 0u, 0u, 0u}};
+  if (signs) {
+    for (int i = 0; i < d; ++i) {
+      if (signs[i] == -1.0f) sg.bits[i >> 5] |= 1u << (i & 31);
+      else if (signs[i] != 1.0f) return FA2_ERR_INVALID_ARG;
+    }
+  }
+  const size_t x_bytes = (size_t)B * H * N * d * 2, c_bytes = (size_t)B * H * N * d;
+  const size_t s_bytes = (size_t)B * H * sizeof(float);
+  const void* bufs[4] = {x, codes, scales, workspace};
+  const size_t sz[4] = {x_bytes, c_bytes, s_bytes, need};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(bufs[i], sz[i], bufs[j], sz[j])) return FA2_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+  fa2::Fp8PackArgs a;
+  a.x = x; a.BH = B * H; a.N = N; a.d = d;
+  a.rotate = signs != nullptr;
+  a.signs = sg;
+  a.codes = codes; a.scales = scales; a.partial = static_cast<float*>(workspace);
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return fa2::launch_fp8_pack(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+int fa2_fwd_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v,
+                void* o, float* lse, int B, int H, int H_kv, int N, int d, int causal, float scale, void* stream,
+                int o_dtype) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v || !o || !lse) return FA2_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA2_ERR_INVALID_ARG;
+  if (H_kv < 1 || H < 1 || H % H_kv != 0 || !is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
+  const int st = check_sizes(B, H, N, d, FA2_BF16);
+  if (st != FA2_OK) return st;
+  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4))
+    return FA2_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * N, kv_rows = (size_t)B * H_kv * N;
+  const void* ins[5] = {q8, k8, v, q_scale, k_scale};
+  const size_t in_sz[5] = {rows * d, kv_rows * d, kv_rows * d * 2, (size_t)B * H * 4, (size_t)B * H_kv * 4};
+  const size_t o_bytes = rows * d * (o_dtype == FA2_BF16 ? 2 : 4), lse_bytes = rows * 4;
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(o, o_bytes, ins[i], in_sz[i]) || overlaps(lse, lse_bytes, ins[i], in_sz[i])) return FA2_ERR_INVALID_ARG;
+  if (overlaps(o, o_bytes, lse, lse_bytes)) return FA2_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+  fa2::FwdArgs a;
+  a.q = q8; a.k = k8; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.Hkv = H_kv;
+  a.causal = causal != 0;
+  a.wl = -1;
+  a.wr = causal ? 0 : -1;
+  a.scale = scale;
+  a.o_bf16 = (o_dtype == FA2_BF16);
+  a.poison = false;
+  a.fp8 = true;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  return fa2::launch_fwd_bf16(a) == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
 int fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d,
             int causal, float scale, void* stream, int in_dtype, int o_dtype, int grad_dtype) {

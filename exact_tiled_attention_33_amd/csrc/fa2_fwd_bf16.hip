@@ -61,6 +61,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -72,7 +73,7 @@ constexpr int kBc = kBf16BlockCols;     // keys per K/V tile
 constexpr int kThreads = kWaves * 64;
 constexpr int kRing = 3;                // K and V tiles resident per ring
 
-template <int D>
+template <int D, bool FP8K = false>
 struct Geo {
   // LDS rows are padded so that every operand read is free of bank conflicts
   // and every per-lane address is one base register plus an immediate:
@@ -81,13 +82,17 @@ struct Geo {
   //    over 16 distinct 16-byte slots of a 256-byte bank line;
   //  * V (stride 2*D + 64 bytes): a half-wave transposing read touches 4
   //    rows x 64 bytes, which the 64-byte pad puts on 4 disjoint quarters.
+  //  (FP8 mode: K rows are D bytes of E4M3 codes, stride D + 16; the same
+  //  16-slot argument holds for its 16-byte reads)
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kStrideK = kRowBytes + 16;
+  static constexpr int kRowBytesK = FP8K ? D : D * 2;
+  static constexpr int kStrideK = kRowBytesK + 16;
   static constexpr int kStrideV = kRowBytes + 64;
   static constexpr int kTileK = kBc * kStrideK;
   static constexpr int kTileV = kBc * kStrideV;
   static constexpr int kLdsBytes = kRing * (kTileK + kTileV);
   static constexpr int kChunks = kRowBytes / 16;            // 16-byte data chunks per row
+  static constexpr int kChunksK = kRowBytesK / 16;
   // A tile is copied by 64-lane instructions that each fill 64 consecutive
   // 16-byte LDS slots (pad slots included); instruction i goes to wave i % 8.
   static constexpr int kSlotsK = kStrideK / 16;              // 16-byte slots per K row
@@ -214,15 +219,16 @@ __device__ __forceinline__ T pin(T x) {
 // the correction is what keeps the answer exact.
 constexpr float kTileSumLimit = 2147483648.0f;  // 2^31
 
-template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED>
+template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED, bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
                      int BH, int N, int T, float c, int poison, int group, int wl, int wr,
                      const SplitItem* __restrict__ items, float* __restrict__ part, int n_slots, int part_rows,
                      const int* __restrict__ sp_ptr, const unsigned* __restrict__ sp_ent, int n_layouts,
-                     int n_entries, PagedArgs pg) {
-  using G = Geo<D>;
+                     int n_entries, PagedArgs pg, const float* __restrict__ qsc,
+                     const float* __restrict__ ksc) {
+  using G = Geo<D, FP8>;
   // K tiles 0, 1 then V tiles 0, 1 (2-deep rings)
   __shared__ __attribute__((aligned(1024))) char smem[G::kLdsBytes];
   char* const lds_k = smem;
@@ -282,8 +288,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // grouped key/value heads: `group` consecutive query heads share one
   // (paged: the cache base; the head is part of each tile's address)
   const long long kv_head = PAGED ? 0 : (long long)(bh / group) * N * D;
-  const __bf16* kh = k + kv_head;
-  const __bf16* vh = v + kv_head;
+  // FP8: q and k hold E4M3 codes (one byte each) of the rotated Q and K with
+  // one scale per (sequence, head); the MFMA sums code products, so the two
+  // scales join the exp2 multiplier
+  if constexpr (FP8) c = c * qsc[bh] * ksc[bh / group];
+  const char* const kh = (const char*)k + kv_head * (FP8 ? 1 : 2);
+  const char* const vh = (const char*)(v + kv_head);
 
   // Rows: the two wavefronts of a SIMD take adjacent 32-row slices, so the
   // causal work of the two groups stays balanced.
@@ -295,7 +305,17 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // head-dim slice 16*s + 8*half .. +7), held for the whole key loop.
   // Rows past N read as zeros.
   bf16x8 qf[G::kKSteps];
-  {
+  i32x8 qf8[D / 64];  // FP8: query = lane % 32, codes of dims 64*s + 32*half .. +31
+  if constexpr (FP8) {
+    const int rows = max(0, min(kRows, nq_rows - qw));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)q + head + (long long)min(qw, nq_rows) * D, rows * D);
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s) {
+      const u32x4 lo = load16(rq, l32 * D + 64 * s + 32 * half);
+      const u32x4 hi = load16(rq, l32 * D + 64 * s + 32 * half + 16);
+      qf8[s] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  } else {
     const int rows = max(0, min(kRows, nq_rows - qw));
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head + (long long)min(qw, nq_rows) * D, rows * D * 2);
 #pragma unroll
@@ -388,6 +408,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // bytes between consecutive keys in global memory (paged cache:
   // [page, slot, kv head, d], so H_kv rows of d apart)
   const int row_bytes = PAGED ? pg.kv_heads * G::kRowBytes : G::kRowBytes;
+  const int row_bytes_k = PAGED ? row_bytes : G::kRowBytesK;
   constexpr int kCopyK = (G::kInstK + kWaves - 1) / kWaves;
   constexpr int kCopyV = (G::kInstV + kWaves - 1) / kWaves;
   int voff_k[kCopyK], voff_v[kCopyV];
@@ -395,7 +416,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   for (int k = 0; k < kCopyK; ++k) {
     const int u = (wave + k * kWaves) * 64 + lane;
     const int chunk = u % G::kSlotsK;
-    voff_k[k] = (u / G::kSlotsK) * row_bytes + (chunk < G::kChunks ? chunk : 0) * 16;
+    voff_k[k] = (u / G::kSlotsK) * row_bytes_k + (chunk < G::kChunksK ? chunk : 0) * 16;
   }
 #pragma unroll
   for (int k = 0; k < kCopyV; ++k) {
@@ -405,17 +426,18 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
   const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
   const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
-  auto copy_tile = [&](const __bf16* src, int slot, int j, auto is_k) __attribute__((always_inline)) {
+  auto copy_tile = [&](const char* src, int slot, int j, auto is_k) __attribute__((always_inline)) {
     constexpr bool K_TILE = decltype(is_k)::value;
     constexpr int kInst = K_TILE ? G::kInstK : G::kInstV;
     constexpr int kCopy = K_TILE ? kCopyK : kCopyV;
     const int key0 = tile_of(j) * kBc;
     const int rows = min(kBc, n_keys - key0);
-    long long src_off = (long long)key0 * D;
+    const int rb = K_TILE ? row_bytes_k : row_bytes;  // bytes between keys
+    long long src_off = (long long)key0 * (K_TILE ? G::kRowBytesK : G::kRowBytes);
     if constexpr (PAGED) {
       // a tile lies in one page (page_size is a multiple of kBc)
       const int page = min(max(page_row[key0 / pg.page_size], 0), pg.n_pages - 1);
-      src_off = ((long long)page * pg.page_size + key0 % pg.page_size) * pg.kv_heads * D + (long long)kvh * D;
+      src_off = (((long long)page * pg.page_size + key0 % pg.page_size) * pg.kv_heads * D + (long long)kvh * D) * 2;
     }
     const unsigned long long gsrc = uniform_addr(src + src_off);
     const unsigned base = (K_TILE ? lds_k0 + slot * G::kTileK : lds_v0 + slot * G::kTileV);
@@ -440,7 +462,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     for (int k = 0; k < kCopy; ++k) {
       if (wave + k * kWaves < kInst) {
         int vo = K_TILE ? voff_k[k] : voff_v[k];
-        if (ragged) vo = min(vo / row_bytes, rows - 1) * row_bytes + vo % row_bytes;
+        if (ragged) vo = min(vo / rb, rows - 1) * rb + vo % rb;
         copy16_to_lds(gsrc, vo, base + k * kWaves * 1024);
       }
     }
@@ -457,6 +479,19 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int k_lane = l32 * G::kStrideK + 16 * half;
   const int v_lane = (4 * half + ((lane & 15) >> 2)) * G::kStrideV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   auto k_off = [&](int kb, int s) __attribute__((always_inline)) { return k_lane + 32 * kb * G::kStrideK + 32 * s; };
+  // FP8 K operand (kb, s): row 32*kb + l32, codes of dims 64*s + 32*half .. +31
+  const int k_lane8 = l32 * G::kStrideK + 32 * half;
+  auto k_off8 = [&](int kb, int s) __attribute__((always_inline)) { return k_lane8 + 32 * kb * G::kStrideK + 64 * s; };
+  auto read_k8 = [&](const char* kbuf, int kb, int s) __attribute__((always_inline)) {
+    const u32x4 lo = *(const u32x4*)(kbuf + k_off8(kb, s));
+    const u32x4 hi = *(const u32x4*)(kbuf + k_off8(kb, s) + 16);
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E4M3 (format 0) and
+  // unit block scales (E8M0 127 = 2^0)
+  auto mfma_fp8 = [&](i32x8 a, i32x8 b, f32x16 acc) __attribute__((always_inline)) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+  };
   auto v_off = [&](int db, int kb, int h, int u) __attribute__((always_inline)) { return v_lane + (32 * kb + 16 * h + 8 * u) * G::kStrideV + 64 * db; };
 
   f32x16 oacc[G::kDBlocks];
@@ -483,6 +518,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // computed but fully masked in the vector phase, so their P is 0.
   // Operands are read from LDS kAhead MFMAs ahead of their use.
   auto scores_mfma = [&](const char* kbuf) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int n = 0; n < 2 * (D / 64); ++n)
+        sacc[n & 1] = mfma_fp8(read_k8(kbuf, n & 1, n >> 1), qf8[n >> 1], n < 2 ? f32x16{} : sacc[n & 1]);
+      return;
+    }
     // MFMA n uses k-step s = n / 2 of block kb = n % 2 (two independent chains).
     constexpr int kN = 2 * G::kKSteps;
     auto read_k = [&](int n) __attribute__((always_inline)) { return *(const bf16x8*)(kbuf + k_off(n & 1, n >> 1)); };
@@ -524,8 +565,64 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // 16 MFMAs of S_j and the 16 of O^T += V_{j-1}^T P_{j-1}^T form one stream
   // whose operand reads run kAhead MFMAs ahead across the boundary between
   // the two products, so the first O^T MFMA does not wait for a fresh read.
+  // FP8: the stream is made of 16-byte operand units: 2 per score MFMA
+  // (the halves of its 32-byte K operand), then one per O^T MFMA (as in the
+  // bf16 stream); units are read kAhead ahead of their consumer.
+  auto matrix_phase_fp8 = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    constexpr int kNS8 = 2 * (D / 64);    // score MFMAs (K = 64)
+    constexpr int kNP = 4 * G::kDBlocks;  // MFMAs of O^T
+    constexpr int kU = 2 * kNS8 + kNP;    // operand units
+    const char* kbuf = lds_k + S * G::kTileK;
+    const char* vbuf = lds_v + ((S + kRing - 1) % kRing) * G::kTileV;
+    auto read_unit = [&](int u) __attribute__((always_inline)) {
+      if (u < 2 * kNS8) {
+        const int n = u >> 1;
+        return *(const u32x4*)(kbuf + k_off8(n & 1, n >> 1) + 16 * (u & 1));
+      }
+      const int m = u - 2 * kNS8, db = m % G::kDBlocks, kb = (m / G::kDBlocks) >> 1, h = (m / G::kDBlocks) & 1;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbuf + v_off(db, kb, h, 0)));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbuf + v_off(db, kb, h, 1)));
+      return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    __builtin_amdgcn_s_setprio(1);
+    u32x4 op[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) op[u] = read_unit(u);
+    u32x4 first_half = {};
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const u32x4 a = op[u % kAhead];
+      if (u + kAhead < kU) op[u % kAhead] = read_unit(u + kAhead);
+      if (u < 2 * kNS8) {
+        if ((u & 1) == 0) {
+          first_half = a;
+        } else {
+          const int n = u >> 1;
+          const i32x8 a8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(first_half, a, 0, 1, 2, 3, 4, 5, 6, 7));
+          sacc[n & 1] = mfma_fp8(a8, qf8[n >> 1], n < 2 ? negm : sacc[n & 1]);
+        }
+      } else {
+        const int m = u - 2 * kNS8, db = m % G::kDBlocks, ks = m / G::kDBlocks;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pk[ks >> 1][ks & 1],
+                                                          oacc[db], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) sched_ds_reads(u < 2 * kNS8 ? 1 : 2);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (u >= 2 * kNS8 || (u & 1)) __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (u + kAhead < kU) sched_ds_reads(u + kAhead < 2 * kNS8 ? 1 : 2);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
   auto matrix_phase = [&](auto slot) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
+    if constexpr (FP8) {
+      matrix_phase_fp8(slot);
+      return;
+    }
     constexpr int kNS = 2 * G::kKSteps;   // MFMAs of S_j
     constexpr int kNP = 4 * G::kDBlocks;  // MFMAs of O^T
     const char* kbuf = lds_k + S * G::kTileK;
@@ -820,7 +917,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (half == 0) lse[(long long)bh * nq_rows + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
 }
 
-template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED = false>
+template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED = false, bool FP8 = false>
 hipError_t launch_t(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)(a.items ? a.n_items : T) * a.B * a.H;
@@ -829,11 +926,11 @@ hipError_t launch_t(const FwdArgs& a) {
   // exactly 0 even for scale == 0; any c that small already makes every
   // probability exactly 1 in fp32.
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16, SPARSE, PAGED>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16, SPARSE, PAGED, FP8>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
                      a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr,
                      (const SplitItem*)a.items, (float*)a.part, a.n_slots, kBr, a.sp_ptr, a.sp_ent,
-                     a.n_layouts, a.n_entries, PagedArgs{});
+                     a.n_layouts, a.n_entries, PagedArgs{}, a.q_scale, a.k_scale);
   return hipGetLastError();
 }
 
@@ -846,6 +943,11 @@ hipError_t launch_s(const FwdArgs& a) {
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a) {
+  if (a.fp8) {
+    if (a.wl >= 0 || a.wr >= 0)
+      return a.o_bf16 ? launch_t<D, true, true, false, false, true>(a) : launch_t<D, true, false, false, false, true>(a);
+    return a.o_bf16 ? launch_t<D, false, true, false, false, true>(a) : launch_t<D, false, false, false, false, true>(a);
+  }
   return a.sp_ptr ? launch_s<D, true>(a) : launch_s<D, false>(a);
 }
 
@@ -981,10 +1083,11 @@ hipError_t launch_paged_t(const FwdArgs& a) {
   const long long grid = (long long)a.n_slots * groups;
   if (grid > 0x7fffffffLL || grid < 1) return hipErrorInvalidValue;
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, groups, a.N,
                      1, c, a.poison ? 1 : 0, a.H / a.Hkv, -1, -1, (const SplitItem*)nullptr, (float*)a.part,
-                     a.n_slots, nq_rows, (const int*)nullptr, (const unsigned*)nullptr, 1, 0, a.paged);
+                     a.n_slots, nq_rows, (const int*)nullptr, (const unsigned*)nullptr, 1, 0, a.paged,
+                     (const float*)nullptr, (const float*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, OUT_BF16>), dim3((unsigned)groups), dim3(kMergeThreads), 0, a.stream,

@@ -63,6 +63,11 @@ struct FwdArgs {
   // Paged decoding (launch_decode_paged): n_q new tokens per sequence, N =
   // the largest context; n_slots = chunks per (sequence, key/value head).
   PagedArgs paged;
+  // FP8 forward (bf16 kernel's FP8 mode): q and k hold E4M3 codes, one fp32
+  // scale per (b, h) in q_scale[B*H] and per (b, kv head) in k_scale.
+  bool fp8 = false;
+  const float* q_scale = nullptr;
+  const float* k_scale = nullptr;
   hipStream_t stream;
 };
 
@@ -107,6 +112,26 @@ constexpr int kBwdQRows = kBwdQWaves * 32;  // 256
 constexpr int kBwdQCols = 64;
 constexpr int kBwdKVKeys = 128;
 constexpr int kBwdKVRows = 32;
+
+// Signs of the FP8 rotation: bit i set = coordinate i negated (d <= 128).
+struct Fp8Signs {
+  unsigned bits[4];
+};
+
+// FP8 packing of one [BH][N][d] bf16 tensor (fa2_fp8.hip).
+struct Fp8PackArgs {
+  const void* x;
+  int BH, N, d;
+  bool rotate;
+  Fp8Signs signs;
+  void* codes;      // [BH][N][d] E4M3 codes
+  float* scales;    // [BH]
+  float* partial;   // workspace: [BH][fp8_pack_chunks(N)] chunk maxima
+  hipStream_t stream;
+};
+
+int fp8_pack_chunks(int N);
+hipError_t launch_fp8_pack(const Fp8PackArgs& a);
 
 // Enqueue the merge of split partial results into O and LSE (after the
 // forward kernel, on the same stream).

@@ -465,6 +465,66 @@ int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, vo
                      void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype);
 
 /*
+ * fa2_fp8_pack_workspace -- workspace bytes of fa2_fp8_pack for [B, H, N, .]
+ * (B*H*ceil(N/256) floats).  Host-only.  FA2_OK or FA2_ERR_INVALID_ARG.
+ */
+int fa2_fp8_pack_workspace(int B, int H, int N, size_t* workspace_bytes);
+
+/*
+ * fa2_fp8_pack -- rotate and quantize Q (or K) for fa2_fwd_fp8.
+ *
+ * Each row x (d values) becomes x R with R = diag(signs) H / sqrt(d), H the
+ * Sylvester-Hadamard matrix, computed in fp32 in a fixed order: signs, then
+ * butterfly stages h = 1, 2, ..., d/2 replacing (a, b) at (i, i + h) of
+ * every 2h-block by (a + b, a - b), then one multiply by the fp32 constant
+ * 1/sqrt(d).  Each (b, h) block of rotated values is quantized to OCP E4M3
+ * (largest finite 448) with scale = amax / 448: codes = E4M3(clamp(x R *
+ * (448 / amax), -448, 448)), rounded to nearest even; a block of zeros gets
+ * codes 0 and scale 1.
+ *
+ * Source: Mishra, "FlashAttention-2 and -3: From Algebra to GPU
+ * Scheduling", "Low precision changes numerical error": a shared orthogonal
+ * mixing transform spreads outliers before quantization and leaves QK^T
+ * unchanged in exact arithmetic ((QR)(KR)^T = QK^T); block scaling governs
+ * the quantization error.  Use the same signs for Q and K.
+ *
+ *   x          device bf16 [B, H, N, d] (d 64 or 128, else UNSUPPORTED).
+ *   signs      HOST array of d values, each +1 or -1 (else
+ *              FA2_ERR_INVALID_ARG); NULL = no rotation (plain per-block
+ *              quantization).
+ *   codes      device [B, H, N, d] bytes, 16-byte aligned; overwritten.
+ *   scales     device fp32 [B, H]; overwritten.
+ *   workspace  device, >= fa2_fp8_pack_workspace bytes.
+ * Buffers must not overlap.  Returns FA2_OK after enqueueing two kernels on
+ * `stream`, else a negative fa2_status.
+ */
+int fa2_fp8_pack(const void* x, int B, int H, int N, int d, const float* signs, void* codes, float* scales,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa2_fwd_fp8 -- the forward pass with Q K^T on FP8 matrix cores.
+ *
+ * q8, k8 are fa2_fp8_pack outputs (E4M3 codes of the rotated Q and K, with
+ * q_scale [B, H] and k_scale [B, H_kv]); v is bf16.  The kernel computes
+ * S = scale * q_scale * k_scale * (codes_q . codes_k) with E4M3 x E4M3
+ * products accumulated in fp32 (v_mfma_scale_f32_32x32x64_f8f6f4), then
+ * the same online softmax, bf16 P V product and outputs as fa2_fwd_gqa.
+ * Relative to exact attention the result carries the quantization error of
+ * Q and K (bounded per score by scale * sum_d (|q_d| e(k_d) + e(q_d) |k_d| +
+ * e(q_d) e(k_d)), e(x) = max(2^-4 |x|, 2^-10 * block scale)); relative to
+ * exact attention of the dequantized codes it carries only fa2_fwd's
+ * rounding.
+ *
+ *   q8 [B, H, N, d], k8 [B, H_kv, N, d] device bytes, 16-byte aligned.
+ *   v [B, H_kv, N, d] device bf16; o, lse, B, H, H_kv, N, d, causal, scale,
+ *   stream, o_dtype as for fa2_fwd_gqa.
+ * Returns FA2_OK after enqueueing, else a negative fa2_status.
+ */
+int fa2_fwd_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v,
+                void* o, float* lse, int B, int H, int H_kv, int N, int d, int causal, float scale, void* stream,
+                int o_dtype);
+
+/*
  * fa2_plan_t -- the launch geometry fa2_fwd uses (or would use) for a shape,
  * for reporting and tests.  Host-only; touches no device.
  */

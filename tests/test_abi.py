@@ -21,7 +21,7 @@ HEADER = ROOT / "include" / "fa2.h"
 def _declared_functions():
     text = HEADER.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa2_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa2_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_expected_entry_points():

@@ -1,0 +1,154 @@
+"""GPU parity of the FP8 forward pass with incoherent processing.
+
+* fa2_fp8_pack against the oracle's pack_fp8: the E4M3 codes and the fp32
+  scales bit for bit (byte work), with and without rotation, d = 64 and 128,
+  ragged lengths, outliers.
+* fa2_fwd_fp8 against the oracle's attention of the dequantized codes,
+  every element, at the bf16 forward bars (|O| <= 1e-2, |LSE| <= 1e-3 with
+  fp32 O; plus half a bf16 ulp for bf16 O): the kernel's only differences
+  from that definition are its fp32 accumulation and bf16 P.
+* The quantization error budget against exact attention (the derived
+  per-row score bound), and the effect the pages state: the mixing rotation
+  lowers the error on inputs with outliers.
+* long_causal at full size on sampled rows.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_33_amd as fa2
+import oracle.exact_attention as ex
+import oracle.fp8_attention as f8
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _np32(t):
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def _bf16_half_ulp(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
+
+
+def _inputs(B, H, H_kv, N, d, seed, outliers=False):
+    w = workloads.get("long_causal").with_(B=B, H=H, N=N, d=d, outlier_frac=0.001 if outliers else 0.0)
+    q, k, v = workloads.make_inputs(w, seed)
+    return q, k[:, :H_kv].contiguous(), v[:, :H_kv].contiguous()
+
+
+PACK = [(2, 3, 700, 128, True, True), (1, 2, 300, 64, True, False), (1, 2, 513, 128, False, True),
+        (1, 1, 1, 128, True, False)]
+
+
+@pytest.mark.parametrize("B,H,N,d,rotate,outliers", PACK,
+                         ids=[f"{b}x{h}x{n}x{d}-{'rot' if r else 'plain'}{'-outl' if o else ''}"
+                              for b, h, n, d, r, o in PACK])
+def test_pack_codes_and_scales_bit_exact(B, H, N, d, rotate, outliers):
+    x, _, _ = _inputs(B, H, H, N, d, seed=1700 + N, outliers=outliers)
+    signs = workloads.make_signs(d, 5) if rotate else None
+    print(f"[case] fp8 pack {B}x{H}x{N}x{d} rotate={rotate}", flush=True)
+    codes, scales = fa2.fp8_pack(x.to(DEV), signs)
+    torch.cuda.synchronize()
+    ec, es = f8.pack_fp8(_np32(x), signs if rotate else np.ones(d), rotate)
+    got = codes.cpu().numpy()
+    bad = int(np.sum(got != ec))
+    print(f"[fp8 pack] code mismatches: {bad} of {got.size}", flush=True)
+    assert bad == 0
+    assert np.array_equal(scales.cpu().numpy(), es)
+
+
+FWD = [
+    # B, H, H_kv, N, d, causal, outliers, o_bf16
+    (1, 2, 2, 700, 128, True, True, False),
+    (1, 2, 2, 700, 128, False, False, False),
+    (2, 4, 2, 333, 128, True, False, True),
+    (1, 2, 2, 513, 64, True, True, False),
+    (1, 3, 1, 129, 64, False, False, True),
+    (1, 1, 1, 1, 128, True, False, False),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,causal,outliers,o_bf16", FWD,
+                         ids=[f"{b}x{h}/{hk}x{n}x{d}-{'causal' if c else 'full'}{'-outl' if o else ''}{'-bf16o' if ob else ''}"
+                              for b, h, hk, n, d, c, o, ob in FWD])
+def test_fwd_fp8_matches_dequantized_attention(B, H, H_kv, N, d, causal, outliers, o_bf16):
+    q, k, v = _inputs(B, H, H_kv, N, d, seed=1800 + N, outliers=outliers)
+    signs = workloads.make_signs(d, 6)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[case] fp8 fwd {B}x{H}/{H_kv}x{N}x{d} causal={causal}", flush=True)
+    o_dtype = torch.bfloat16 if o_bf16 else torch.float32
+    o, lse = fa2.forward_fp8(q.to(DEV), k.to(DEV), v.to(DEV), signs, causal=causal, scale=scale, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    eo, el = f8.attention_ref_fp8(_np32(q), _np32(k), _np64(v), scale, causal, signs)
+    o, lse = _np64(o), _np64(lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    err_o = np.abs(o - eo)
+    err_l = float(np.max(np.abs(lse - el)))
+    print(f"[fp8 fwd] max|dO|={float(np.max(err_o)):.3e} max|dLSE|={err_l:.3e}", flush=True)
+    assert np.all(err_o <= 1e-2 + (_bf16_half_ulp(eo) if o_bf16 else 0.0))
+    assert err_l <= 1e-3
+
+
+def test_fp8_error_budget_and_rotation_benefit():
+    """Against exact attention: every row within the derived budget, and the
+    rotation lowers the error on inputs with outliers."""
+    B, H, N, d = 1, 4, 1024, 128
+    q, k, v = _inputs(B, H, H, N, d, seed=1901, outliers=True)
+    signs = workloads.make_signs(d, 7)
+    scale = 1.0 / math.sqrt(d)
+    print("[case] fp8 error budget 1x4x1024x128 causal with outliers", flush=True)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_rot, l_rot = fa2.forward_fp8(qd, kd, vd, signs, causal=True, scale=scale)
+    o_pl, l_pl = fa2.forward_fp8(qd, kd, vd, None, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    eo, el = ex.attention_ref(_np64(q), _np64(k), _np64(v), scale, True)
+    bound = f8.score_error_bound(_np32(q), _np32(k), scale, True, signs, True)
+    vmax = float(np.max(np.abs(_np64(v))))
+    err_l = np.abs(_np64(l_rot) - el)
+    err_o = np.abs(_np64(o_rot) - eo).max(axis=-1)
+    assert np.all(err_l <= bound + 1e-3)
+    assert np.all(err_o <= (np.exp(2 * bound) - 1) * vmax + 1e-2)
+    e_rot = float(np.mean(err_l))
+    e_pl = float(np.mean(np.abs(_np64(l_pl) - el)))
+    eo_rot = float(np.mean(np.abs(_np64(o_rot) - eo)))
+    eo_pl = float(np.mean(np.abs(_np64(o_pl) - eo)))
+    print(f"[fp8 budget] mean|dLSE| rotated {e_rot:.3e} plain {e_pl:.3e}; mean|dO| rotated {eo_rot:.3e} "
+          f"plain {eo_pl:.3e}; max|dLSE| {float(err_l.max()):.3e} (bound max {float(bound.max()):.3e})", flush=True)
+    assert e_rot < e_pl and eo_rot < eo_pl
+
+
+def test_fp8_headline_workload_sampled_rows():
+    w = workloads.get("long_causal")
+    print(f"[case] fp8 fwd {w.name} {w.shape}, sampled rows", flush=True)
+    q, k, v = workloads.make_inputs(w, 0, device=DEV)
+    signs = workloads.make_signs(w.d, 8)
+    o, lse = fa2.forward_fp8(q, k, v, signs, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(9)
+    rows = np.array(sorted({0, 1, 255, 256, w.N - 1, *rng.integers(0, w.N, size=30).tolist()}))
+    for b, h in ((0, 0), (w.B - 1, w.H - 1), (1, 7)):
+        qc, qs = f8.pack_fp8(_np32(q[b:b + 1, h:h + 1]), signs)
+        kc, ks = f8.pack_fp8(_np32(k[b:b + 1, h:h + 1]), signs)
+        qdq = f8.e4m3_decode(qc[0, 0]) * float(qs[0, 0])
+        kdq = f8.e4m3_decode(kc[0, 0]) * float(ks[0, 0])
+        eo, el = ex.attention_rows(qdq, kdq, _np64(v[b, h]), w.scale, True, rows)
+        err_o = float(np.max(np.abs(_np64(o[b, h][rows]) - eo)))
+        err_l = float(np.max(np.abs(_np64(lse[b, h][rows]) - el)))
+        print(f"[fp8 fwd] head ({b},{h}) {len(rows)} rows: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+        assert err_o <= 1e-2 and err_l <= 1e-3

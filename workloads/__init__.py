@@ -192,3 +192,10 @@ def make_paged_cache(context_lens, H_kv: int, d: int, page_size: int, seed: int,
         table[b, :n] = perm[nxt:nxt + n].to(torch.int32)
         nxt += n
     return k.to(device), v.to(device), table.to(device)
+
+
+def make_signs(d: int, seed: int):
+    """Seeded random +-1 vector of length d (float32 numpy array), the
+    signs of the FP8 rotation."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randint(0, 2, (d,), generator=g) * 2 - 1).to(torch.float32).numpy()
