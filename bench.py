@@ -46,6 +46,13 @@ from one fa2_fwd call made before timing; throughput is credited backward
 work (10*B*H*N^2*d, halved when causal) and the CPU baseline times the fp64
 gradient oracle.
 
+With --fp8 (forward) a step is fa2_fp8_pack of Q and of K (rotation by a
+seeded randomized Hadamard transform and E4M3 quantization, one scale per
+(sequence, head)) followed by fa2_fwd_fp8 (Q K^T on FP8 matrix cores, P V in
+bf16); `value` counts the whole step, the roofline the attention kernel
+alone against the peak of its mix of work (half the flops at the FP8 rate,
+half at the bf16 rate: 2 / (1/5033 + 1/2517) TFLOP/s).
+
 With --pass decode a step is one fa2_decode_paged call on a synthetic
 serving batch (DECODE_CONFIG: B sequences whose context lengths are drawn
 uniformly from [L_min, L_max] by a seeded generator, one new token each,
@@ -80,6 +87,8 @@ METRIC_BWD = "attention bwd TFLOPs/s and % of MI355X bf16 MFMA peak, d=128 N=8k 
 # Dense bf16 matrix-core peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_F32_TFLOPS = 157.3
+# Dense FP8 matrix-core peak (E4M3 x E4M3, fp32 accumulation): twice bf16.
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 PEAK_HBM_GBS = 8000.0
 BWD_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_bwd_bf16.hip",
                "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
@@ -198,7 +207,7 @@ def run_bench(args) -> dict:
     call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  w.B, w.H, hkv, w.N, w.d, wl, wr, w.scale, handle, in_code, o_code)
     schedule = {"split": False}
-    if args.split == "auto" and w.dtype == "bf16" and args.block_sparse is None:
+    if args.split == "auto" and w.dtype == "bf16" and args.block_sparse is None and not args.fp8:
         splan = fa2.split_plan(w.shape, window=(wl, wr), num_units=props.multi_processor_count)
         if splan.splits:
             items = splan.device_items(dev)
@@ -211,6 +220,34 @@ def run_bench(args) -> dict:
                         "workspace_bytes": splan.workspace_bytes}
     fwd_call = fa2.fa2_fwd_split if schedule["split"] else fa2.fa2_fwd_window
     sparse_pairs = None
+    fp8_kernel = None
+    if args.fp8:
+        if args.window is not None or args.block_sparse is not None or w.dtype != "bf16":
+            raise SystemExit("bench.py: --fp8 takes a bf16 workload, causal or not, and no other variant")
+        signs = workloads.make_signs(w.d, args.seed + 11)
+        sg = [float(t) for t in signs.tolist()]
+        q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+        qs = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        ks = torch.empty(k.shape[:2], dtype=torch.float32, device=dev)
+        wsq = torch.empty(fa2.fa2_fp8_pack_workspace(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+        wsk = torch.empty(fa2.fa2_fp8_pack_workspace(w.B, hkv, w.N), dtype=torch.uint8, device=dev)
+        attn_args = (q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), v.data_ptr(), o.data_ptr(),
+                     lse.data_ptr(), w.B, w.H, hkv, w.N, w.d, int(w.causal), w.scale, handle, o_code)
+
+        def fwd_call(*_):
+            st = fa2.fa2_fp8_pack(q.data_ptr(), w.B, w.H, w.N, w.d, sg, q8.data_ptr(), qs.data_ptr(), wsq.data_ptr(),
+                                  wsq.numel(), handle)
+            if st == fa2.FA2_OK:
+                st = fa2.fa2_fp8_pack(k.data_ptr(), w.B, hkv, w.N, w.d, sg, k8.data_ptr(), ks.data_ptr(),
+                                      wsk.data_ptr(), wsk.numel(), handle)
+            if st == fa2.FA2_OK:
+                st = fa2.fa2_fwd_fp8(*attn_args)
+            return st
+
+        fp8_kernel = lambda: fa2.fa2_fwd_fp8(*attn_args)  # noqa: E731
+        schedule = {"split": False, "fp8": {"rotation": "randomized Hadamard", "format": "E4M3",
+                                            "scales": "one per (sequence, head)"}}
     if args.block_sparse is not None:
         if args.window is not None or w.dtype != "bf16":
             raise SystemExit("bench.py: --block-sparse takes a bf16 workload and no --window")
@@ -261,8 +298,25 @@ def run_bench(args) -> dict:
         flops = 4.0 * w.B * w.H * w.d * workloads.credited_pairs(w.N, wl, wr)
     value = flops * args.steps / wall / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    fp8_timing = None
+    if fp8_kernel is not None:
+        # the attention kernel alone, on the packed inputs of the last step
+        ks_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ke_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            ks_ev[i].record(stream)
+            if fp8_kernel() != fa2.FA2_OK:
+                raise fa2.Fa2Error(-1, "fa2_fwd_fp8")
+            ke_ev[i].record(stream)
+        torch.cuda.synchronize()
+        step_ms = avg_launch_ms
+        avg_launch_ms = sum(a.elapsed_time(b) for a, b in zip(ks_ev, ke_ev)) / args.steps
+        peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+        fp8_timing = {"step_ms_avg": round(step_ms, 4), "attention_kernel_ms_avg": round(avg_launch_ms, 4),
+                      "pack_ms_avg": round(step_ms - avg_launch_ms, 4)}
     traffic = (traffic_from_profiles(w.name)
-               if hkv == w.H and args.window is None and not schedule["split"] and sparse_pairs is None else None)
+               if hkv == w.H and args.window is None and not schedule["split"] and sparse_pairs is None
+               and fp8_kernel is None else None)
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
     # Algorithmic bytes per launch: Q, K, V read once, O and LSE written once.
     esz = 2 if w.dtype == "bf16" else 4
@@ -301,6 +355,7 @@ def run_bench(args) -> dict:
             "dropout": 0.0, "backward": False, "parallelism": "single GPU",
         },
         "schedule": schedule,
+        **({"fp8_timing": fp8_timing} if fp8_timing else {}),
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {
             **roof,
@@ -321,7 +376,7 @@ def run_bench(args) -> dict:
         "kernel_source_sha256_16": kernel_source_hash(),
         "context_not_target": "pages (A100): FA1 25-40% of peak, FA2 50-73% of peak, up to 230 TFLOP/s",
     }
-    if not args.no_cpu_baseline and args.window is None and sparse_pairs is None:
+    if not args.no_cpu_baseline and args.window is None and sparse_pairs is None and fp8_kernel is None:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, budget_s=args.cpu_budget)
     return result
 
@@ -588,6 +643,8 @@ def main() -> int:
                     help="forward: split heavy query tiles' key ranges when the planner predicts a gain")
     ap.add_argument("--block-sparse", type=float, default=None, metavar="DENSITY",
                     help="forward: random 128x128 block mask per head with this block density")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward: FP8 Q K^T with incoherent processing (pack Q, K, then fa2_fwd_fp8)")
     ap.add_argument("--sparse-block", type=int, nargs=2, default=[128, 128], metavar=("ROWS", "KEYS"),
                     help="block size of the --block-sparse mask (rows a multiple of 32, keys of 64)")
     ap.add_argument("--split-keys", type=int, default=0,
