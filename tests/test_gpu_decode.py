@@ -115,3 +115,32 @@ def test_decode_rejections_on_gpu():
     with pytest.raises(fa2.Fa2Error) as e:
         fa2.decode_paged(torch.randn((1, 4, 130, 128)).to(torch.bfloat16).to(DEV), kd, vd, td, ctx, max_context=100)
     assert e.value.status == fa2.FA2_ERR_UNSUPPORTED  # 2 x 130 query rows per key/value head
+
+
+def test_decode_benchmark_batch_sampled_heads():
+    """The serving batch the benchmark times (64 sequences, seeded context
+    lengths in [1024, 8192], 32 query heads on 8 key/value heads, 64-key
+    pages in a permuted cache, the library's chunk size): six (sequence,
+    head) pairs against the oracle's page-table gather and causal mask."""
+    g = torch.Generator().manual_seed(0)
+    B, H, Hkv, d, page = 64, 32, 8, 128, 64
+    lens = torch.randint(1024, 8193, (B,), generator=g).tolist()
+    kc, vc, table = workloads.make_paged_cache(lens, Hkv, d, page, seed=1)
+    q = torch.randn((B, H, 1, d), generator=g).to(torch.bfloat16)
+    print(f"[case] decode benchmark batch: {B} sequences, {sum(lens)} keys", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa2.decode_paged(q.to(DEV), kc.to(DEV), vc.to(DEV), table.to(DEV),
+                              torch.tensor(lens, dtype=torch.int32, device=DEV), max_context=max(lens), scale=scale)
+    torch.cuda.synchronize()
+    K, V, T = _np64(kc), _np64(vc), table.numpy()
+    for b, h in ((0, 0), (63, 31), (17, 5), (40, 12), (5, 30), (33, 3)):
+        L = lens[b]
+        kv = ref.kv_head_of(h, H, Hkv)
+        kb = ref.gather_pages(K, T[b], L, kv)
+        vb = ref.gather_pages(V, T[b], L, kv)
+        m, l, num = ref.softmax_stats(ref.scores(_np64(q[b, h]), kb, scale), ref.visible_decode(1, L), vb)
+        eo, el = ref.finalize(m, l, num)
+        err_o = float(np.max(np.abs(_np64(o[b, h]) - eo)))
+        err_l = float(np.max(np.abs(_np64(lse[b, h]) - el)))
+        print(f"[decode] ({b},{h}) L={L}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+        assert err_o <= 1e-2 and err_l <= 1e-3

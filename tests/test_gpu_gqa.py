@@ -126,3 +126,24 @@ def test_gqa_backward_every_element(B, H, H_kv, N, causal, outliers):
         ratio = float(np.max(err / np.maximum(m, 1e-30)))
         print(f"[gqa bwd] {name}: max|err|={float(np.max(err)):.3e} max err/m={ratio:.2e}", flush=True)
         assert np.all(err <= 2.0 ** -6 * m + 1e-6 * float(np.max(m))), f"{name} exceeds the bound"
+
+
+def test_gqa_headline_size_sampled_rows():
+    """long_causal at full size with 4 key/value heads (the configuration
+    `bench.py --kv-heads 4` times): sampled rows of three query heads,
+    each against its group's key/value head."""
+    w = workloads.get("long_causal")
+    print(f"[case] gqa fwd {w.name} {w.shape} with 4 key/value heads, sampled rows", flush=True)
+    q, k, v = workloads.make_inputs(w, 0, device=DEV)
+    k, v = k[:, :4].contiguous(), v[:, :4].contiguous()
+    o, lse = fa2.forward(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(14)
+    rows = np.array(sorted({0, 255, 256, w.N - 1, *rng.integers(0, w.N, size=30).tolist()}))
+    for b, h in ((0, 0), (1, 15), (0, 6)):
+        g = ref.kv_head_of(h, w.H, 4)
+        eo, el = ref.attention_rows(_np64(q[b, h]), _np64(k[b, g]), _np64(v[b, g]), w.scale, True, rows)
+        err_o = float(np.max(np.abs(_np64(o[b, h][rows]) - eo)))
+        err_l = float(np.max(np.abs(_np64(lse[b, h][rows]) - el)))
+        print(f"[gqa fwd] head ({b},{h}) -> kv {g}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+        assert err_o <= 1e-2 and err_l <= 1e-3

@@ -120,3 +120,29 @@ def test_sparse_rejections_on_gpu():
         fa2.forward_sparse(q.float(), k.float(), v.float(), good)
     with pytest.raises(ValueError):
         fa2.forward_sparse(q[:, :, :500].contiguous(), k[:, :, :500].contiguous(), v[:, :, :500].contiguous(), good)
+
+
+def test_sparse_headline_size_sampled_rows():
+    """long_causal at full size with the masks the benchmark times (one
+    seeded mask of 128x128 blocks per head, density 0.3, causal): sampled
+    rows of three heads against the oracle's definition."""
+    w = workloads.get("long_causal")
+    print(f"[case] sparse {w.name} {w.shape} 128x128 blocks p=0.3, sampled rows", flush=True)
+    q, k, v = workloads.make_inputs(w, 0, device=DEV)
+    nb = -(-w.N // 128)
+    bm = workloads.make_block_mask(w.H, nb, nb, 0.3, seed=0)
+    plan = fa2.fa2_sparse_plan(w.N, 128, 128, bm, w.causal)
+    o, lse = fa2.forward_sparse(q, k, v, plan, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    rows = np.array(sorted({0, 127, 128, 255, 256, w.N - 1, *rng.integers(0, w.N, size=30).tolist()}))
+    for b, h in ((0, 0), (1, 15), (1, 4)):
+        Q, K, V = _np64(q[b, h]), _np64(k[b, h]), _np64(v[b, h])
+        s = ref.scores(Q[rows], K, w.scale)
+        vis = ref.visible_block_sparse(rows, np.arange(w.N), bm[h], 128, 128, w.causal)
+        m, l, num = ref.softmax_stats(s, vis, V)
+        eo, el = ref.finalize(m, l, num)
+        err_o = float(np.max(np.abs(_np64(o[b, h][rows]) - eo)))
+        err_l = float(np.max(np.abs(_np64(lse[b, h][rows]) - el)))
+        print(f"[sparse] head ({b},{h}): max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+        assert err_o <= 1e-2 and err_l <= 1e-3
