@@ -1083,12 +1083,18 @@ hipError_t launch_paged_t(const FwdArgs& a) {
   const long long grid = (long long)a.n_slots * groups;
   if (grid > 0x7fffffffLL || grid < 1) return hipErrorInvalidValue;
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, groups, a.N,
-                     1, c, a.poison ? 1 : 0, a.H / a.Hkv, -1, -1, (const SplitItem*)nullptr, (float*)a.part,
-                     a.n_slots, nq_rows, (const int*)nullptr, (const unsigned*)nullptr, 1, 0, a.paged,
-                     (const float*)nullptr, (const float*)nullptr);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (nq_rows <= 32) {
+    // a group fits one wavefront: the lighter one-wavefront-per-chunk kernel
+    e = launch_decode_waves(a);
+  } else {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, groups, a.N,
+                       1, c, a.poison ? 1 : 0, a.H / a.Hkv, -1, -1, (const SplitItem*)nullptr, (float*)a.part,
+                       a.n_slots, nq_rows, (const int*)nullptr, (const unsigned*)nullptr, 1, 0, a.paged,
+                       (const float*)nullptr, (const float*)nullptr);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D, OUT_BF16>), dim3((unsigned)groups), dim3(kMergeThreads), 0, a.stream,
                      (const float*)a.part, a.o, a.lse, a.paged, groups, nq_rows, a.n_slots, a.N);

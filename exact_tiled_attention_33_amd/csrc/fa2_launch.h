@@ -140,6 +140,10 @@ hipError_t launch_split_merge(const FwdArgs& a);
 // Enqueue paged decoding: the chunk kernel, then the merge of its partials.
 hipError_t launch_decode_paged(const FwdArgs& a);
 
+// The chunk kernel of paged decoding with one wavefront per (chunk, group)
+// (fa2_decode.hip), for groups of at most 32 query rows.
+hipError_t launch_decode_waves(const FwdArgs& a);
+
 // Enqueue the backward kernels (D, dK/dV, dQ) for bf16 inputs.
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 
