@@ -285,16 +285,27 @@ int fa2_split_plan(int B, int H, int N, int d, int window_left, int window_right
   if (max_chunk_tiles > 0) {
     slots = make_schedule(ranges, max_chunk_tiles, &plan);
   } else {
-    // candidates: no split, and chunks of about total / (k * units) key tiles
+    // candidates: no split; chunks of about total / (k * units) key tiles
+    // (k workgroups per unit); and chunks that cut the longest band into s
+    // equal parts
     slots = make_schedule(ranges, 0, &plan);
     const double whole = schedule_cost(plan, slots, bh, num_units);
-    long long total = 0;
-    for (const KeyRange& r : ranges) total += r.hi - r.lo;
+    long long total = 0, longest = 0;
+    for (const KeyRange& r : ranges) {
+      total += r.hi - r.lo;
+      longest = std::max<long long>(longest, r.hi - r.lo);
+    }
     total *= bh;
+    std::vector<long long> chunks;
+    for (int k4 : {4, 5, 6, 7, 8, 10, 12, 16, 24, 32}) {  // k = k4 / 4
+      chunks.push_back((4 * total + (long long)k4 * num_units - 1) / ((long long)k4 * num_units));
+    }
+    for (int parts = 2; parts <= 8; ++parts) chunks.push_back((longest + parts - 1) / parts);
+    std::sort(chunks.begin(), chunks.end());
+    chunks.erase(std::unique(chunks.begin(), chunks.end()), chunks.end());
     double best = whole * kSplitMinGain;
-    for (int kk : {1, 2, 3, 4, 6, 8}) {
-      const long long c = std::max<long long>(kMinChunkTiles, (total + (long long)kk * num_units - 1) /
-                                                                  ((long long)kk * num_units));
+    for (const long long c0 : chunks) {
+      const long long c = std::max<long long>(kMinChunkTiles, c0);
       if (c > (1 << 30)) continue;
       std::vector<fa2_split_item> cand;
       const int cs = make_schedule(ranges, (int)c, &cand);

@@ -258,7 +258,9 @@ typedef struct fa2_split_item {
  * Each query tile's visible key tiles (the band of fa2_fwd_window) are cut
  * into chunks of at most C key tiles; chunks are listed longest first (the
  * order the hardware dispatches them in).  With max_chunk_tiles == 0 the
- * library picks C, or no split at all, by simulating the dispatch of the
+ * library picks C (among chunks of about total/(k*num_units) for k from 1
+ * to 8 and those that cut the longest band into 2..8 equal parts), or no
+ * split at all, by simulating the dispatch of the
  * B*H*n_items workgroups on `num_units` compute units (one resident
  * workgroup each) under a cost model of the kernels: a per-workgroup
  * start-up cost, one unit per key tile, and the traffic of writing and
