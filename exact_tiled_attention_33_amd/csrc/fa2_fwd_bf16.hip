@@ -80,14 +80,17 @@ struct Geo {
   //  * K (stride 2*D + 16 bytes): the 16 lanes of a b128 read phase read 16
   //    consecutive rows at the same column, which the 16-byte pad spreads
   //    over 16 distinct 16-byte slots of a 256-byte bank line;
-  //  * V (stride 2*D + 64 bytes): a half-wave transposing read touches 4
-  //    rows x 64 bytes, which the 64-byte pad puts on 4 disjoint quarters.
+  //  * V (stride 2*D, no pad): a half-wave transposing read touches 4
+  //    consecutive rows x 64 bytes at one column; the 64-byte units of a row
+  //    are stored XOR-permuted by a function of the row (vswz), which puts
+  //    the 4 rows on 4 disjoint quarters of the bank line.  No pad means a
+  //    V tile is 2*D 64-lane copy instructions rather than 2.5*D.
   //  (FP8 mode: K rows are D bytes of E4M3 codes, stride D + 16; the same
   //  16-slot argument holds for its 16-byte reads)
   static constexpr int kRowBytes = D * 2;
   static constexpr int kRowBytesK = FP8K ? D : D * 2;
   static constexpr int kStrideK = kRowBytesK + 16;
-  static constexpr int kStrideV = kRowBytes + 64;
+  static constexpr int kStrideV = kRowBytes;
   static constexpr int kTileK = kBc * kStrideK;
   static constexpr int kTileV = kBc * kStrideV;
   static constexpr int kLdsBytes = kRing * (kTileK + kTileV);
@@ -102,6 +105,11 @@ struct Geo {
   static_assert(kBc * kSlotsK % 64 == 0 && kBc * kSlotsV % 64 == 0, "tiles must fill whole instructions");
   static constexpr int kKSteps = D / 16;                    // k-steps of the score MFMA
   static constexpr int kDBlocks = D / 32;                   // 32-row blocks of O^T
+  // V row r keeps its 64-byte unit q (32 head dims) at unit q ^ vswz(r).
+  // D = 128 (4 units, rows 256 bytes apart): rows r..r+3 need 4 distinct
+  // units, vswz = r % 4.  D = 64 (2 units, 128-byte rows, two rows per
+  // 256-byte bank line): rows r and r+2 share a half line, vswz = (r/2) % 2.
+  static __device__ __forceinline__ int vswz(int r) { return D == 128 ? (r & 3) : ((r >> 1) & 1); }
 };
 
 __device__ __forceinline__ float max_halves(float x) {
@@ -400,9 +408,10 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   // Tile copies: instruction i of a tile fills LDS slots [64i, 64i + 64);
-  // slot u is (row u / slots-per-row, chunk u % slots-per-row), and the
-  // lanes that land on a row's pad slots fetch that row's chunk 0 (any
-  // in-range address would do).  Keys past N read as zeros.  Instruction i
+  // slot u is (row u / slots-per-row, chunk u % slots-per-row); in K the
+  // lanes that land on a row's pad slot fetch that row's chunk 0 (any
+  // in-range address would do), in V each slot fetches the chunk the row's
+  // unit permutation puts there.  Instruction i
   // is issued by wave i % 8; the per-lane source offsets do not depend on
   // the tile and are computed once.
   // bytes between consecutive keys in global memory (paged cache:
@@ -420,9 +429,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 #pragma unroll
   for (int k = 0; k < kCopyV; ++k) {
+    // V slot u holds row u / kChunks, stored unit (u % kChunks) / 4, which is
+    // the row's global unit (u % kChunks) / 4 ^ vswz(row)
     const int u = (wave + k * kWaves) * 64 + lane;
-    const int chunk = u % G::kSlotsV;
-    voff_v[k] = (u / G::kSlotsV) * row_bytes + (chunk < G::kChunks ? chunk : 0) * 16;
+    const int row = u / G::kSlotsV, chunk = (u % G::kSlotsV) ^ (4 * G::vswz(row));
+    voff_v[k] = row * row_bytes + chunk * 16;
   }
   const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
   const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
@@ -477,7 +488,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // (i / 4) of a 4-row slab and dcol 4*(i % 4) of a 16-column slab; lane i
   // then receives the 4 keys of one dcol (lane % 32).
   const int k_lane = l32 * G::kStrideK + 16 * half;
-  const int v_lane = (4 * half + ((lane & 15) >> 2)) * G::kStrideV + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // V: the lane's row within an 8-row slab is 4*half + (lane%16)/4; every
+  // slab starts at a multiple of 8 rows, so vswz of the row is the lane's
+  // own, and O^T block db (64-byte unit db) of the row sits at unit db ^ vswz.
+  const int v_row = 4 * half + ((lane & 15) >> 2);
+  const int v_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  int v_lane[G::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < G::kDBlocks; ++db) v_lane[db] = v_row * G::kStrideV + v_col + 64 * (db ^ G::vswz(v_row));
   auto k_off = [&](int kb, int s) __attribute__((always_inline)) { return k_lane + 32 * kb * G::kStrideK + 32 * s; };
   // FP8 K operand (kb, s): row 32*kb + l32, codes of dims 64*s + 32*half .. +31
   const int k_lane8 = l32 * G::kStrideK + 32 * half;
@@ -492,7 +510,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   auto mfma_fp8 = [&](i32x8 a, i32x8 b, f32x16 acc) __attribute__((always_inline)) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
   };
-  auto v_off = [&](int db, int kb, int h, int u) __attribute__((always_inline)) { return v_lane + (32 * kb + 16 * h + 8 * u) * G::kStrideV + 64 * db; };
+  auto v_off = [&](int db, int kb, int h, int u) __attribute__((always_inline)) { return v_lane[db] + (32 * kb + 16 * h + 8 * u) * G::kStrideV; };
 
   f32x16 oacc[G::kDBlocks];
 #pragma unroll
@@ -722,7 +740,11 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       t = (part[0] + part[1]) + (part[2] + part[3]);
       tb = partb[0] + partb[1];
     };
-    probs(std::false_type{}, 0.f);
+    // Until some row of the wavefront has its reference (normally: the
+    // wavefront's first key tile) every row takes the max path below, which
+    // computes P itself; the pass against m = 0 would be thrown away.
+    t = 0.f;
+    if (__builtin_amdgcn_ballot_w64(m_set)) probs(std::false_type{}, 0.f);
     if (__builtin_amdgcn_ballot_w64(!m_set || !(t <= kTileSumLimit))) {
       // Row max of S - m in four independent chains (chain r takes the
       // elements e = 16*kb + i with e % 4 == r), then both halves of the row.
