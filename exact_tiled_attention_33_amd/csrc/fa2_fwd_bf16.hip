@@ -264,7 +264,14 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // query heads (rows bh*nq_rows .. +nq_rows of q, o, lse: the heads of a
   // group are consecutive) against key tiles c*chunk_tiles .. +chunk_tiles
   // of the sequence's cache, and always writes a partial result (slot c).
-  const int bh = blockIdx.x % BH;
+  // Without a mask every query tile of a head does the same work; then,
+  // when the heads come in multiples of 8, consecutive workgroups of one
+  // XCD (blockIdx.x = x + 8r goes to XCD x) take the T tiles of one head
+  // together, so the head's K and V are fetched into that XCD's L2 once
+  // and read from there by its other tiles.
+  const bool xcd_major = !MASKED && !SPARSE && !PAGED && items == nullptr && (BH & 7) == 0;
+  const int xcd_r = (int)(blockIdx.x >> 3);
+  const int bh = xcd_major ? (xcd_r / T) * 8 + (int)(blockIdx.x & 7) : (int)(blockIdx.x % BH);
   int t, ck_lo = 0, ck_hi = 1 << 30, slot = -1;
   int n_keys = N;         // keys this head attends over
   int nq_rows = N;        // query rows of this head (or group)
@@ -287,6 +294,8 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     ck_lo = max(it.kt_lo, 0);
     ck_hi = it.kt_hi;
     slot = it.slot < n_slots ? it.slot : -1;
+  } else if (xcd_major) {
+    t = xcd_r % T;
   } else {
     const int tr = blockIdx.x / BH;
     t = MASKED ? (T - 1 - tr) : tr;
