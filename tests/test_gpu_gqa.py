@@ -45,6 +45,9 @@ FWD = [
     (1, 6, 3, 520, 64, "bf16", True, False),
     (1, 4, 2, 100, 64, "fp32", True, False),
     (1, 4, 4, 130, 128, "bf16", True, False),
+    # unmasked, B*H a multiple of 8 (XCD-major tile order with grouped heads)
+    (2, 8, 2, 600, 128, "bf16", False, True),
+    (1, 16, 4, 300, 64, "bf16", False, False),
 ]
 
 

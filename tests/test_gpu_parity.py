@@ -80,6 +80,9 @@ SMALL = [
     (1, 1, 1, 64, "fp32", False), (1, 1, 3, 128, "fp32", True),
     (1, 2, 127, 64, "fp32", True), (1, 1, 129, 128, "fp32", False),
     (1, 2, 1000, 64, "fp32", False), (1, 1, 1000, 128, "fp32", True),
+    # unmasked with B*H a multiple of 8: the XCD-major tile order
+    (2, 4, 300, 64, "bf16", False), (1, 8, 777, 128, "bf16", False),
+    (2, 8, 513, 64, "bf16", False), (4, 4, 256, 128, "bf16", False),
 ]
 
 
@@ -247,7 +250,8 @@ def test_error_status_on_gpu():
 # poison is always overwritten first, so the result is bit-identical to the
 # ordinary run.
 
-POISON_CASES = [(1, 2, 1000, 64, True), (2, 3, 777, 128, False), (1, 4, 1024, 128, True)]
+POISON_CASES = [(1, 2, 1000, 64, True), (2, 3, 777, 128, False), (1, 4, 1024, 128, True),
+                (2, 4, 600, 64, False), (1, 8, 700, 128, False)]
 
 
 @pytest.mark.parametrize("B,H,N,d,causal", POISON_CASES,
