@@ -6,9 +6,12 @@
 A step is one fa2_fwd call over one batch of the workload (default: the
 headline workload, long_causal = bf16 [B=2, H=16, N=8192, d=128], causal,
 0.1% of Q/K entries x20, fp32 O).  Inputs are seeded, synthetic and already
-resident in device memory when timing starts.  W untimed steps, then K
-timed steps bracketed by device synchronisation; each launch is also
-bracketed by HIP events recorded on the stream the kernel runs on.
+resident in device memory when timing starts; successive steps rotate over
+copies of the inputs and outputs that together span at least 512 MB (twice
+the 256 MB last-level cache), so each step reads its inputs from HBM.  W
+untimed steps, then K timed steps bracketed by device synchronisation; each
+launch is also bracketed by HIP events recorded on the stream the kernel
+runs on.
 
 Prints ONE JSON line: throughput in TFLOP/s of credited work
 (4*B*H*N^2*d, halved when causal), the roofline of the attention kernel
@@ -75,6 +78,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -98,6 +102,7 @@ KERNEL_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_fwd_bf16.hip",
                   "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
                   "exact_tiled_attention_33_amd/csrc/fa2_launch.h"]
 CALIB_BYTES = 1 << 30
+ROTATE_BYTES = 512 * 10**6  # rotated input/output sets span at least this (twice the 256 MB MALL)
 METRIC_DECODE = "paged-KV decode, GB/s of key/value traffic vs MI355X HBM peak"
 DECODE_CONFIG = {"B": 64, "H": 32, "H_kv": 8, "d": 128, "n_q": 1, "page_size": 64, "L_min": 1024, "L_max": 8192}
 
@@ -265,16 +270,26 @@ def run_bench(args) -> dict:
         schedule = {"split": False, "block_sparse": {"block": [bq, bk], "density": args.block_sparse,
                                                      "layouts": w.H, "key_tile_entries": sp.n_entries,
                                                      "visible_pair_fraction": round(sparse_pairs / dense_pairs, 4)}}
+    # Successive steps rotate over copies of (Q, K, V, O, LSE) that together
+    # exceed the 256 MB last-level cache (MALL) twice over, so that no step
+    # finds its inputs left in that cache by the previous one and the bytes
+    # moved are HBM bytes.  (The FP8 step packs from one Q, K into one code
+    # buffer, so it keeps a single set.)
+    set_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse))
+    n_sets = 1 if fp8_kernel is not None else min(8, max(1, -(-ROTATE_BYTES // set_bytes)))
+    sets = [(q, k, v, o, lse)] + [(q.clone(), k.clone(), v.clone(), torch.empty_like(o), torch.empty_like(lse))
+                                  for _ in range(n_sets - 1)]
+    set_args = [tuple(t.data_ptr() for t in st) + tuple(call_args[5:]) for st in sets]
     torch.cuda.synchronize()
 
-    def step():
-        st = fwd_call(*call_args)
+    def step(i):
+        st = fwd_call(*set_args[i % n_sets])
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st)
 
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
+        for i in range(args.warmup):
+            step(i)
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -282,7 +297,7 @@ def run_bench(args) -> dict:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        step()
+        step(args.warmup + i)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -370,7 +385,9 @@ def run_bench(args) -> dict:
         },
         "timing": {"events_span_ms": round(span_ms, 4), "wall_s": round(wall, 4),
                    "per_launch_ms_min": round(min(per_launch_ms), 4),
-                   "per_launch_ms_max": round(max(per_launch_ms), 4)},
+                   "per_launch_ms_median": round(statistics.median(per_launch_ms), 4),
+                   "per_launch_ms_max": round(max(per_launch_ms), 4),
+                   "input_sets": n_sets, "input_set_bytes": set_bytes},
         "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count},
         "kernel_source_sha256_16": kernel_source_hash(),
