@@ -84,7 +84,8 @@ struct Geo {
   //    consecutive rows x 64 bytes at one column; the 64-byte units of a row
   //    are stored XOR-permuted by a function of the row (vswz), which puts
   //    the 4 rows on 4 disjoint quarters of the bank line.  No pad means a
-  //    V tile is 2*D 64-lane copy instructions rather than 2.5*D.
+  //    V tile is D/8 copy instructions (64 lanes x 16 bytes) rather than
+  //    D/8 + 4.
   //  (FP8 mode: K rows are D bytes of E4M3 codes, stride D + 16; the same
   //  16-slot argument holds for its 16-byte reads)
   static constexpr int kRowBytes = D * 2;
