@@ -329,9 +329,18 @@ def run_bench(args) -> dict:
         peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
         fp8_timing = {"step_ms_avg": round(step_ms, 4), "attention_kernel_ms_avg": round(avg_launch_ms, 4),
                       "pack_ms_avg": round(step_ms - avg_launch_ms, 4)}
-    traffic = (traffic_from_profiles(w.name)
-               if hkv == w.H and args.window is None and not schedule["split"] and sparse_pairs is None
-               and fp8_kernel is None else None)
+    plain_run = (hkv == w.H and args.window is None and not schedule["split"] and sparse_pairs is None
+                 and fp8_kernel is None)
+    traffic = traffic_from_profiles(w.name) if plain_run else None
+    prof = os.path.join("profiles", f"fa2_fwd_{w.name}_hbm.md")
+    if traffic is not None:
+        traffic_source = prof
+    elif not plain_run:
+        traffic_source = "none: counters are taken for the plain forward of the workload only"
+    elif not os.path.exists(os.path.join(ROOT, prof)):
+        traffic_source = f"none: no {prof}"
+    else:
+        traffic_source = f"none: the kernel sources changed since {prof} was measured"
     plan = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), in_code)
     # Algorithmic bytes per launch: Q, K, V read once, O and LSE written once.
     esz = 2 if w.dtype == "bf16" else 4
@@ -375,6 +384,7 @@ def run_bench(args) -> dict:
         "roofline": {
             **roof,
             "traffic": traffic,
+            "traffic_source": traffic_source,
             "kernel_ms_avg": round(avg_launch_ms, 4),
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": alg_bytes,
