@@ -41,7 +41,7 @@ int check_sizes(int B, int H, int N, int d, int in_dtype) {
 
 void own_tiles(int in_dtype, int* rows, int* cols, int* waves) {
   if (in_dtype == FA2_BF16) {
-    *rows = fa2::kBf16BlockRows; *cols = fa2::kBf16BlockCols; *waves = fa2::kBf16Waves;
+    *rows = fa2::kFwdBlockRows; *cols = fa2::kBf16BlockCols; *waves = fa2::kFwdWaves;
   } else {
     *rows = fa2::kF32BlockRows; *cols = fa2::kF32BlockCols; *waves = fa2::kF32Waves;
   }

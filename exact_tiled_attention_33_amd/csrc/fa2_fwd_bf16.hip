@@ -1,4 +1,17 @@
-// FlashAttention-2 forward for bf16 inputs on gfx950 (MI355X).
+// FlashAttention-2 forward for bf16 inputs on gfx950 (MI355X): two kernels.
+//
+//  * fwd_kernel (plain, causal and sliding-window attention, also with
+//    grouped key/value heads): 128-row query tiles on workgroups of four
+//    wavefronts, two workgroups per compute unit, and ONE interleaved
+//    MFMA/softmax instruction stream per wavefront and key tile.  Its own
+//    comment block below gives the schedule.
+//  * fwd_bf16_kernel (the split schedule's chunks, block-sparse lists, paged
+//    decoding and the FP8 mode): 256-row query tiles on workgroups of eight
+//    wavefronts in two groups that alternate matrix and vector phases.
+//
+// The products, layouts and online softmax described next are shared by
+// both; the work decomposition and schedule paragraphs describe
+// fwd_bf16_kernel.
 //
 // Work decomposition (Saraf, "FlashAttention 2: Three Places the Chip Was
 // Still Waiting", sections 2.3 and 2.4): one workgroup per query tile of 256
@@ -949,6 +962,439 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (half == 0) lse[(long long)bh * nq_rows + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
 }
 
+// ---- the forward kernel (plain, causal and sliding-window masks) ------------
+// Workgroups of 4 wavefronts (one per SIMD) own 128 query rows of one
+// (batch, head), each wavefront 32 of them; two such workgroups share a
+// compute unit, so the two wavefronts of a SIMD come from different
+// workgroups and never wait for each other.
+//
+// Each wavefront runs ONE instruction stream per key tile j: the 16 MFMAs of
+// O^T += V_{j-1}^T P_{j-1}^T, then the 16 of S_{j+1} = K_{j+1} Q^T, and after
+// each MFMA a few VALU instructions of the softmax of S_j (the scores the
+// previous tile's stream computed): the vector work of a tile runs in the
+// shadow of the wavefront's own matrix work (Mishra, "FlashAttention-3:
+// overlap work on Hopper": matrix operations interleaved with softmax work;
+// "A pipeline is constrained by its slowest stage").  On gfx950 a wavefront
+// that only issues MFMAs starves the VALU instructions of the other
+// wavefront of its SIMD, so the overlap has to happen inside each stream.
+//
+// K and V tiles of 64 keys live in 2-deep LDS rings (slot = tile % 2).  The
+// stream of tile j copies K_{j+2} and V_j (global -> LDS, spread over its
+// first MFMAs) into the slots of K_j and V_{j-2}, which nobody reads after
+// the barrier that starts tile j; the barrier at the end of tile j, after
+// each wavefront's wait for its own copies, publishes them.
+constexpr int kRing2 = 2;               // K (and V) tiles resident per ring
+constexpr int kW4 = kFwdWaves;          // wavefronts per workgroup (one per SIMD)
+constexpr int kBr4 = kFwdBlockRows;     // query rows per workgroup
+constexpr int kThreads4 = kW4 * 64;
+constexpr int kAheadIL = 3;             // LDS operand reads in flight ahead of the MFMAs
+static_assert(kBr4 == kW4 * kRows, "each wavefront owns 32 query rows");
+template <int D, bool MASKED, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads4, kThreads4), amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+               void* __restrict__ o, float* __restrict__ lse, int BH, int N, int T, float c, int poison, int group,
+               int wl, int wr) {
+  using G = Geo<D, false>;
+  __shared__ __attribute__((aligned(1024))) char smem[kRing2 * (G::kTileK + G::kTileV)];
+  char* const lds_k = smem;
+  char* const lds_v = smem + kRing2 * G::kTileK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // Grid: workgroup -> (batch*head, query tile); causal and window tiles are
+  // issued heaviest (latest rows) first; without a mask and with heads in
+  // multiples of 8, consecutive workgroups of one XCD (blockIdx.x = x + 8r
+  // goes to XCD x) take the T tiles of one head, so its K and V are fetched
+  // into that XCD's L2 once.
+  const bool xcd_major = !MASKED && (BH & 7) == 0;
+  const int xcd_r = (int)(blockIdx.x >> 3);
+  const int bh = xcd_major ? (xcd_r / T) * 8 + (int)(blockIdx.x & 7) : (int)(blockIdx.x % BH);
+  const int t = xcd_major ? xcd_r % T : (MASKED ? (T - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH));
+  const int n_keys = N;
+  const long long head = (long long)bh * N * D;
+  const long long kv_head = (long long)(bh / group) * N * D;
+  const char* const kh = (const char*)(k + kv_head);
+  const char* const vh = (const char*)(v + kv_head);
+
+  const int q0 = t * kBr4;
+  const int qw = q0 + 32 * wave;
+  const int qrow = qw + l32;
+
+  // Q rows of the wavefront as MFMA B operands, held for the whole key loop;
+  // rows past N read as zeros.
+  bf16x8 qf[G::kKSteps];
+  {
+    const int rows = max(0, min(kRows, N - qw));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head + (long long)min(qw, N) * D, rows * D * 2);
+#pragma unroll
+    for (int s = 0; s < G::kKSteps; ++s) qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (l32 * D + 16 * s + 8 * half) * 2));
+  }
+
+  // Key tiles j_lo .. j_lo + n_tiles - 1 hold a key some row of the
+  // workgroup sees (key j visible to query i iff i - wl <= j <= i + wr, a
+  // negative bound meaning no limit); this wavefront's rows see every key of
+  // tiles jf_lo .. jf_hi - 1, which therefore need no mask.
+  const int nk = (n_keys + kBc - 1) / kBc;
+  int j_lo = 0, n_tiles = nk, jf_lo = 0, jf_hi = n_keys / kBc;
+  if (MASKED) {
+    const int q_last = min(q0 + kBr4, N) - 1;
+    const int w_last = min(qw + kRows, N) - 1;
+    if (wl >= 0) {
+      j_lo = max(0, q0 - wl) / kBc;
+      jf_lo = (max(0, w_last - wl) + kBc - 1) / kBc;
+    }
+    int j_hi = nk;
+    if (wr >= 0) {
+      j_hi = min(nk, (q_last + wr) / kBc + 1);
+      jf_hi = min(jf_hi, qw + wr - (kBc - 1) >= 0 ? (qw + wr - (kBc - 1)) / kBc + 1 : 0);
+    }
+    n_tiles = j_hi - j_lo;
+  }
+  const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
+  const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
+
+  // ---- copies: one instruction = 64 lanes x 16 bytes into 64 consecutive
+  // 16-byte LDS slots; instruction i of a tile is issued by wavefront i % 4
+  // (the layouts and per-lane source offsets are those of the other kernel)
+  constexpr int kCopyK = (G::kInstK + kW4 - 1) / kW4;
+  constexpr int kCopyV = (G::kInstV + kW4 - 1) / kW4;
+  constexpr int kMainK = G::kInstK / kW4, kMainV = G::kInstV / kW4;
+  constexpr int kRemK = G::kInstK % kW4, kRemV = G::kInstV % kW4;
+  constexpr int kNC = kMainK + kMainV;  // copies spread through each tile's stream
+  int voff_k[kCopyK], voff_v[kCopyV];
+#pragma unroll
+  for (int kk = 0; kk < kCopyK; ++kk) {
+    const int u = (wave + kk * kW4) * 64 + lane;
+    const int chunk = u % G::kSlotsK;
+    voff_k[kk] = (u / G::kSlotsK) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
+  }
+#pragma unroll
+  for (int kk = 0; kk < kCopyV; ++kk) {
+    const int u = (wave + kk * kW4) * 64 + lane;
+    const int row = u / G::kSlotsV, chunk = (u % G::kSlotsV) ^ (4 * G::vswz(row));
+    voff_v[kk] = row * G::kRowBytes + chunk * 16;
+  }
+  const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
+  const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
+  // this wavefront's instruction kk of key tile jt into ring slot `slot`.
+  // jt is clamped to the last tile (a copy past the end fetches it again
+  // into a slot nobody reads); rows past N come from row N-1 and are masked.
+  auto copy_k = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
+    const int key0 = (j_lo + min(jt, n_tiles - 1)) * kBc;
+    const int rows = min(kBc, n_keys - key0);
+    const unsigned long long gsrc = uniform_addr(kh + (long long)key0 * G::kRowBytes);
+    const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
+    copy16_to_lds(gsrc, min(voff_k[kk], lim), lds_k0 + slot * G::kTileK + kk * kW4 * 1024);
+  };
+  auto copy_v = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
+    const int key0 = (j_lo + min(jt, n_tiles - 1)) * kBc;
+    const int rows = min(kBc, n_keys - key0);
+    const unsigned long long gsrc = uniform_addr(vh + (long long)key0 * G::kRowBytes);
+    const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
+    copy16_to_lds(gsrc, min(voff_v[kk], lim), lds_v0 + slot * G::kTileV + kk * kW4 * 1024);
+  };
+  // debug: NaN over this wave's destination blocks of the tile-j copies
+  auto poison_slots = [&](int kslot, int vslot) __attribute__((always_inline)) {
+    const u32x4 nan4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+#pragma unroll
+    for (int kk = 0; kk < kCopyK; ++kk)
+      if (wave + kk * kW4 < G::kInstK)
+        *(__attribute__((address_space(3))) u32x4*)(size_t)(lds_k0 + kslot * G::kTileK + kk * kW4 * 1024 + 16 * lane) = nan4;
+#pragma unroll
+    for (int kk = 0; kk < kCopyV; ++kk)
+      if (wave + kk * kW4 < G::kInstV)
+        *(__attribute__((address_space(3))) u32x4*)(size_t)(lds_v0 + vslot * G::kTileV + kk * kW4 * 1024 + 16 * lane) = nan4;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  };
+
+  // ---- LDS operand addresses: a per-lane base register plus an immediate
+  // (ring slots are compile-time constants in the unrolled tile loop)
+  const int k_lane = (int)lds_offset_of(lds_k) + l32 * G::kStrideK + 16 * half;
+  const int v_row = 4 * half + ((lane & 15) >> 2);
+  const int v_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  int v_lane[G::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < G::kDBlocks; ++db)
+    v_lane[db] = (int)lds_offset_of(lds_v) + v_row * G::kStrideV + v_col + 64 * (db ^ G::vswz(v_row));
+
+  f32x16 oacc[G::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  f32x16 sA[2], sB[2];      // score tiles S_j (being turned into P) and S_{j+1} (being computed)
+  u32x4 pk[2][2];           // P as bf16 pairs (P_j, produced by tile j's stream)
+  float m = 0.f, mc = 0.f;  // reference max of the row (raw score units) and m*c
+  bool m_set = false;
+  float l = 0.f, lb = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  constexpr int kNS = 2 * G::kKSteps;   // MFMAs of S
+  constexpr int kNP = 4 * G::kDBlocks;  // MFMAs of O^T
+
+  // One key tile's stream.  HAS_PV: O^T += V_{j-1}^T P_{j-1}^T;  HAS_S:
+  // snext = K_{j+1} Q^T;  SOFT: P_j = exp2(S_j*c - m*c) from scur into pk,
+  // with the row sums of the fp32 and of the bf16-rounded P;  copy_kv: bit 0
+  // K_{j+2}, bit 1 V_j.  The sched_barrier after every MFMA and the empty asm
+  // statements that use each softmax step's results keep the interleave the
+  // source order states (the compiler would otherwise gather the VALU work).
+  auto stream = [&](int j, auto slot, f32x16 (&scur)[2], f32x16 (&snext)[2],
+                    auto has_pv, auto has_s, auto soft, auto copy_kv, float& tsum, float& tbsum) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;  // j % 2
+    constexpr bool HAS_PV = decltype(has_pv)::value, HAS_S = decltype(has_s)::value;
+    constexpr bool SOFT = decltype(soft)::value;
+    constexpr bool COPY_K = decltype(copy_kv)::value & 1, COPY_V = (decltype(copy_kv)::value & 2) != 0;
+    constexpr int kNT = (HAS_PV ? kNP : 0) + (HAS_S ? kNS : 0);
+    constexpr int kKOff = ((SL + 1) % kRing2) * G::kTileK;  // K_{j+1}
+    constexpr int kVOff = ((SL + 1) % kRing2) * G::kTileV;  // V_{j-1}
+    // A operand of stream MFMA n: for n < kNP (HAS_PV) V^T of key step
+    // n / kDBlocks (keys 16*ks .. +15, transposing reads) for O^T block
+    // n % kDBlocks; then K rows 32*(ns & 1) .. +31 at k-step ns / 2
+    auto read_op = [&](int n) __attribute__((always_inline)) {
+      if (HAS_PV && n < kNP) {
+        const int db = n % G::kDBlocks, ks = n / G::kDBlocks, kb = ks >> 1, h = ks & 1;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(v_lane[db] + kVOff + (32 * kb + 16 * h) * G::kStrideV));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(v_lane[db] + kVOff + (32 * kb + 16 * h + 8) * G::kStrideV));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const int ns = n - (HAS_PV ? kNP : 0);
+      return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(k_lane + kKOff + 32 * (ns & 1) * G::kStrideK + 32 * (ns >> 1));
+    };
+    // The softmax as a 3-stage pipeline over the 16 element pairs of a lane
+    // (pair p: block p / 8, elements 2(p % 8) and +1).  Half-step 2u: exp2 of
+    // pair u-1 and the exponent arguments of pair u; half-step 2u+1: sums
+    // and bf16 packing of pair u-2.  36 half-steps, spread over the MFMAs.
+    float xs[2][2], es[2][2];  // [pair parity][element]
+    float part[4] = {0.f, 0.f, 0.f, 0.f}, partb[2] = {0.f, 0.f};
+    auto half_step = [&](int hs) __attribute__((always_inline)) {
+      const int u = hs >> 1;
+      if ((hs & 1) == 0) {
+        if (u >= 1 && u <= 16) {
+          const int pp_ = (u - 1) & 1;
+          es[pp_][0] = __builtin_amdgcn_exp2f(xs[pp_][0]);
+          es[pp_][1] = __builtin_amdgcn_exp2f(xs[pp_][1]);
+          asm volatile("" :: "v"(es[pp_][0]), "v"(es[pp_][1]));  // keep the step at this point of the stream
+        }
+        if (u < 16) {
+          xs[u & 1][0] = fmaf(scur[u >> 3][2 * (u & 7)], c, -mc);
+          xs[u & 1][1] = fmaf(scur[u >> 3][2 * (u & 7) + 1], c, -mc);
+          asm volatile("" :: "v"(xs[u & 1][0]), "v"(xs[u & 1][1]));
+        }
+      } else if (u >= 2) {
+        const int p = u - 2, q_ = p & 1;
+        const int i = 2 * (p & 7);
+        part[i & 3] += es[q_][0];
+        part[(i & 3) + 1] += es[q_][1];
+        const bf16x2 pp = {(__bf16)es[q_][0], (__bf16)es[q_][1]};
+        partb[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, partb[(i >> 1) & 1], false);
+        pk[p >> 3][i >> 3][(i & 7) >> 1] = __builtin_bit_cast(unsigned, pp);
+        asm volatile("" :: "v"(part[i & 3]), "v"(part[(i & 3) + 1]), "v"(partb[(i >> 1) & 1]),
+                     "v"(pk[p >> 3][i >> 3][(i & 7) >> 1]));
+      }
+    };
+    constexpr int kHS = 36;
+    // P_{j-1} as the O += V P MFMAs read it: the softmax overwrites pk with
+    // P_j pair by pair while they run (where every write comes after the
+    // last read of its element the two share registers)
+    u32x4 pprev[2][2];
+#pragma unroll
+    for (int a0 = 0; a0 < 2; ++a0)
+#pragma unroll
+      for (int a1 = 0; a1 < 2; ++a1) pprev[a0][a1] = pk[a0][a1];
+    bf16x8 op[kAheadIL];
+    if constexpr (kNT > 0) {
+#pragma unroll
+      for (int n = 0; n < kAheadIL; ++n) op[n] = read_op(n);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < kNT; ++n) {
+      const bf16x8 a = op[n % kAheadIL];
+      if (n + kAheadIL < kNT) op[n % kAheadIL] = read_op(n + kAheadIL);
+      if (HAS_PV && n < kNP) {
+        const int db = n % G::kDBlocks, ks = n / G::kDBlocks;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pprev[ks >> 1][ks & 1]), oacc[db], 0, 0, 0);
+      } else {
+        const int ns = n - (HAS_PV ? kNP : 0);
+        snext[ns & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ns >> 1], ns < 2 ? f32x16{} : snext[ns & 1], 0, 0, 0);
+      }
+      if constexpr (SOFT) {
+        // half-steps hs with floor(hs * kNT / kHS) == n
+#pragma unroll
+        for (int hs = (n * kHS + kNT - 1) / kNT; hs < ((n + 1) * kHS + kNT - 1) / kNT; ++hs) half_step(hs);
+      }
+#pragma unroll
+      for (int cc = 0; cc < kNC; ++cc)
+        if (n == (kNT * cc) / (2 * kNC)) {
+          if (cc < kMainK) {
+            if constexpr (COPY_K) copy_k(j + 2, SL, cc);
+          } else {
+            if constexpr (COPY_V) copy_v(j, SL, cc - kMainK);
+          }
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SOFT && kNT == 0) {
+#pragma unroll
+      for (int hs = 0; hs < kHS; ++hs) half_step(hs);
+    }
+    if constexpr (SOFT) {
+      tsum = (part[0] + part[1]) + (part[2] + part[3]);
+      tbsum = partb[0] + partb[1];
+    }
+  };
+
+  // Mask of score tile j: only tiles this wavefront's rows do not all see
+  // whole (window / causal edges, the ragged end of the sequence).  Element i
+  // of block kb holds key 64*ja + 32*kb + 8*(i/4) + 4*half + (i%4).
+  auto mask_tile = [&](int j, f32x16 (&sc)[2]) __attribute__((always_inline)) {
+    const int ja = j_lo + j;
+    if (ja < jf_lo || ja >= jf_hi) {
+      const int key0 = ja * kBc;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          sc[kb][i] = (key >= key_lo) & (key <= key_hi) ? sc[kb][i] : -INFINITY;
+        }
+    }
+  };
+  // End of tile j's softmax.  The reference max m of a row moves only when a
+  // half-row's probabilities against it sum past kTileSumLimit (or on the
+  // row's first visible tile): then m takes the row max, l and O^T (which
+  // holds tiles < j) are multiplied by exp2((m_old - m_new)*c), and P_j is
+  // recomputed -- the correction that keeps the result exact (Saraf, section
+  // 2.2).
+  auto settle = [&](f32x16 (&sc)[2], float tt, float tb) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(!m_set || !(tt <= kTileSumLimit))) {
+      auto el = [&](int e) __attribute__((always_inline)) { return sc[e >> 4][e & 15]; };
+      float mx[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx[r] = fmaxf(el(r), el(r + 4));
+#pragma unroll
+      for (int e = 8; e < 32; e += 8)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(fmaxf(mx[r], el(e + r)), el(e + r + 4));
+      const float mt = max_halves(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+      const bool has_key = mt > -INFINITY;
+      const float nm = m_set ? fmaxf(m, mt) : (has_key ? mt : 0.f);
+      const float alpha = m_set ? __builtin_amdgcn_exp2f((m - nm) * c) : 0.f;
+      m_set = m_set || has_key;
+      m = nm;
+      mc = m * c;
+      l *= alpha;
+      lb *= alpha;
+#pragma unroll
+      for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      float part[4] = {0.f, 0.f, 0.f, 0.f}, partb[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][i], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][i + 1], c, -mc));
+          part[i & 3] += p0;
+          part[(i & 3) + 1] += p1;
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          partb[(i >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, partb[(i >> 1) & 1], false);
+          pk[kb][i >> 3][(i & 7) >> 1] = __builtin_bit_cast(unsigned, pp);
+        }
+      tt = (part[0] + part[1]) + (part[2] + part[3]);
+      tb = partb[0] + partb[1];
+    }
+    l += tt;
+    lb += tb;
+  };
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using C0 = std::integral_constant<int, 0>;   // no copies
+  using CV = std::integral_constant<int, 2>;   // V copies only
+  using CKV = std::integral_constant<int, 3>;  // K and V copies
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // all of this wavefront's copy instructions of K tile jt
+  auto copy_k_all = [&](int jt, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < kCopyK; ++kk)
+      if (wave + kk * kW4 < G::kInstK) copy_k(jt, slot, kk);
+  };
+  // ---- prologue: K_0 and K_1 in LDS, S_0 computed
+  copy_k_all(0, 0);
+  copy_k_all(1, 1);
+  wait_vmem(0);
+  __syncthreads();
+  {
+    float d0, d1;
+    stream(-1, S1{}, sB, sA, F_{}, T_{}, F_{}, C0{}, d0, d1);  // "tile -1": S_0 (slot 0) into sA
+  }
+  __syncthreads();  // B_0: nobody reads K_0 any more
+
+  // Key tile j (ring slot SL = j % 2; S_j in sA for even j, sB for odd).
+  auto tile = [&](int j, auto slot, auto has_pv, auto has_s, auto cp) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+    constexpr bool COPY_K = decltype(cp)::value & 1;
+    f32x16 (&scur)[2] = SL ? sB : sA;
+    f32x16 (&snext)[2] = SL ? sA : sB;
+    if (poison) poison_slots(SL, SL);
+    if (COPY_K && kRemK > 0 && wave < kRemK) copy_k(j + 2, SL, kMainK);
+    if (kRemV > 0 && wave < kRemV) copy_v(j, SL, kMainV);
+    mask_tile(j, scur);  // diagonal / window edges, and the ragged last tile
+    float tt, tb;
+    stream(j, slot, scur, snext, has_pv, has_s, T_{}, cp, tt, tb);
+    settle(scur, tt, tb);
+    wait_vmem(0);
+    __syncthreads();  // B_{j+1}
+  };
+  // Tiles past tile 0 go in pairs (ring slots 1, 0); a lone last tile
+  // computes no S and copies no K.  (When the last tile ends a pair it
+  // computes an unused S and its K copy fetches the last tile again.)
+  tile(0, S0{}, F_{}, T_{}, CKV{});
+  int j = 1;
+  for (; j + 1 < n_tiles; j += 2) {
+    tile(j, S1{}, T_{}, T_{}, CKV{});
+    tile(j + 1, S0{}, T_{}, T_{}, CKV{});
+  }
+  if (j < n_tiles) tile(j, S1{}, T_{}, F_{}, CV{});
+  // the last O += V P: P_{n-1} with V_{n-1} (a stream "at tile n")
+  {
+    float d0, d1;
+    if (n_tiles & 1) stream(n_tiles, S1{}, sA, sB, T_{}, F_{}, F_{}, C0{}, d0, d1);
+    else stream(n_tiles, S0{}, sA, sB, T_{}, F_{}, F_{}, C0{}, d0, d1);
+  }
+  wait_vmem(0);
+
+  // ---- finalise: one division per row (by the sum of the rounded P the
+  // products used), then O and LSE = ln2 * (m*c + log2 l)
+  const float lt = sum_halves(l);
+  const float ltb = sum_halves(lb);
+  if (qrow >= N) return;
+  const float inv = ltb > 0.f ? 1.0f / ltb : 0.f;
+  const long long orow = head + (long long)qrow * D;
+#pragma unroll
+  for (int db = 0; db < G::kDBlocks; ++db)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int dcol = 32 * db + 8 * a4 + 4 * half;
+      const float x0 = oacc[db][4 * a4 + 0] * inv, x1 = oacc[db][4 * a4 + 1] * inv;
+      const float x2 = oacc[db][4 * a4 + 2] * inv, x3 = oacc[db][4 * a4 + 3] * inv;
+      if (OUT_BF16) {
+        bf16x4 y = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+        *(u32x2*)((__bf16*)o + orow + dcol) = __builtin_bit_cast(u32x2, y);
+      } else {
+        *(float4*)((float*)o + orow + dcol) = make_float4(x0, x1, x2, x3);
+      }
+    }
+  if (half == 0) lse[(long long)bh * N + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
+}
+
 template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED = false, bool FP8 = false>
 hipError_t launch_t(const FwdArgs& a) {
   const int T = (a.N + kBr - 1) / kBr;
@@ -958,6 +1404,18 @@ hipError_t launch_t(const FwdArgs& a) {
   // exactly 0 even for scale == 0; any c that small already makes every
   // probability exactly 1 in fp32.
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
+  if constexpr (!SPARSE && !PAGED && !FP8) {
+    if (a.items == nullptr) {
+      // plain, causal and sliding-window forward: the 128-row kernel
+      const int T4 = (a.N + kBr4 - 1) / kBr4;
+      const long long grid4 = (long long)T4 * a.B * a.H;
+      if (grid4 > 0x7fffffffLL) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fwd_kernel<D, MASKED, OUT_BF16>), dim3((unsigned)grid4), dim3(kThreads4), 0, a.stream,
+                         (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, a.B * a.H, a.N, T4, c,
+                         a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, MASKED, OUT_BF16, SPARSE, PAGED, FP8>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
                      a.B * a.H, a.N, T, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr,

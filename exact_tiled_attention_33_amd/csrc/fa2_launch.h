@@ -77,6 +77,12 @@ struct FwdArgs {
 constexpr int kBf16Waves = 8;
 constexpr int kBf16BlockRows = kBf16Waves * 32;  // 256
 constexpr int kBf16BlockCols = 64;
+// The forward kernel of fa2_fwd / fa2_fwd_gqa / fa2_fwd_window (bf16 in):
+// workgroups of 4 wavefronts x 32 rows, two per compute unit, the same
+// 64-key tiles.  (The 256-row geometry above serves the split, block-sparse,
+// paged and FP8 modes.)
+constexpr int kFwdWaves = 4;
+constexpr int kFwdBlockRows = kFwdWaves * 32;  // 128
 constexpr int kF32Waves = 4;
 constexpr int kF32BlockRows = kF32Waves * 32;    // 128
 constexpr int kF32BlockCols = 32;

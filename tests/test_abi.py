@@ -151,9 +151,9 @@ def test_pages_score_matrix_size():
 def test_own_plan_for_the_workloads():
     import workloads
     mi355x_cus = 256
-    # bf16: 256-row query tiles; fp32: 128-row query tiles
-    expect_groups = {"fp32_small": 1, "short_seq": 1024, "mid_seq": 1024, "long_causal": 1024,
-                     "long_few_head": 256}
+    # bf16 and fp32 alike: 128-row query tiles
+    expect_groups = {"fp32_small": 1, "short_seq": 2048, "mid_seq": 2048, "long_causal": 2048,
+                     "long_few_head": 512}
     for name, w in workloads.WORKLOADS.items():
         code = fa2.BF16 if w.dtype == "bf16" else fa2.F32
         p = fa2.fa2_plan(w.B, w.H, w.N, w.d, int(w.causal), code, num_units=mi355x_cus)

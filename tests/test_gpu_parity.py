@@ -73,7 +73,8 @@ SMALL = [
     # B, H, N, d, dtype, causal
     (1, 1, 1, 64, "bf16", False), (1, 1, 1, 128, "bf16", True),
     (1, 2, 3, 64, "bf16", True), (2, 1, 3, 128, "bf16", False),
-    (1, 2, 127, 64, "bf16", True), (1, 2, 127, 128, "bf16", False),
+    (1, 2, 127, 64, "bf16", True), (1, 2, 127, 128, "bf16", False), (1, 2, 127, 128, "bf16", True),
+    (1, 2, 200, 128, "bf16", True), (1, 1, 33, 128, "bf16", True),
     (2, 1, 129, 64, "bf16", False), (1, 2, 129, 128, "bf16", True),
     (1, 2, 1000, 64, "bf16", True), (1, 2, 1000, 128, "bf16", False),
     (2, 3, 777, 128, "bf16", True), (1, 1, 2048, 128, "bf16", True),

@@ -8,7 +8,9 @@ element is compared on small shapes with chunks of 1, 2, 3 and 5 key tiles
 (so rows that see no key of a chunk occur), under causal, full, sliding
 windows and grouped heads; the long few-head workload [1, 2, 32768, 128]
 causal is checked on sampled rows with the schedule the planner picks.  A
-schedule that splits nothing must give bitwise what fa2_fwd_window gives.
+schedule that splits nothing must match the oracle and give what
+fa2_fwd_window gives to rounding (fa2_fwd_window runs another kernel, which
+rounds exponent arguments and sums in another order).
 """
 
 from __future__ import annotations
@@ -87,7 +89,7 @@ def test_split_every_element(B, H, H_kv, N, d, wl, wr, chunk, outliers, o_bf16):
     _check(o, lse, eo, el, f"{B}x{H}/{H_kv}x{N}x{d} w({wl},{wr}) chunk {chunk}", o_bf16)
 
 
-def test_unsplit_schedule_is_bitwise_fa2_fwd_window():
+def test_unsplit_schedule_matches_fa2_fwd_window():
     q, k, v = (t.to(DEV) for t in _inputs(1, 3, 3, 900, 128, seed=21, outliers=True))
     print("[case] unsplit schedule vs fa2_fwd_window", flush=True)
     for window in ((-1, 0), (-1, -1), (100, 30)):
@@ -96,7 +98,12 @@ def test_unsplit_schedule_is_bitwise_fa2_fwd_window():
         o1, l1 = fa2.forward(q, k, v, scale=0.09, window=window)
         o2, l2 = fa2.forward_split(q, k, v, plan, scale=0.09, window=window)
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2) and torch.equal(l1, l2), window
+        eo, el = ref.attention_ref_window(_np64(q), _np64(k), _np64(v), 0.09, *window)
+        _check(o2, l2, eo, el, f"unsplit schedule window={window}")
+        d_o = float((o1 - o2).abs().max())
+        d_l = float((l1 - l2).abs().max())
+        print(f"[split] unsplit vs fa2_fwd_window {window}: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}", flush=True)
+        assert d_o <= 4e-3 and d_l <= 1e-4, window
 
 
 def test_split_close_to_unsplit_and_deterministic():
