@@ -262,8 +262,72 @@ def pin_window_grad_finite_differences():
             _close(ref_grads[which], fd, 2e-8, f"window ({wl},{wr}) FD d{'QKV'[which]}")
 
 
+def pin_window_grad_driver_grouped_heads():
+    """The [B, H] sliding-window gradient driver with 4 query heads on 2
+    key/value heads (heads 0, 0, 1, 1) and on 1, windows that differ on the
+    two sides: dQ, dK, dV equal central finite differences of the loss summed
+    over the query heads, each head evaluated by explicit loops on the
+    key/value head it reads -- so a shared head's gradient is the sum over
+    its group."""
+    rng = _rng(2027)
+    n, d, h_ = 4, 2, 1e-6
+    for hkv, groups in ((2, [0, 0, 1, 1]), (1, [0, 0, 0, 0])):
+        q = rng.normal(size=(1, 4, n, d))
+        k, v = rng.normal(size=(1, hkv, n, d)), rng.normal(size=(1, hkv, n, d))
+        g = rng.normal(size=(1, 4, n, d))
+        for wl, wr in ((2, 0), (0, 1), (-1, 1)):
+            def loss(qq, kk, vv):
+                return math.fsum(_loss_loops_window(qq[0, h].tolist(), kk[0, groups[h]].tolist(),
+                                                    vv[0, groups[h]].tolist(), g[0, h].tolist(), 0.8, wl, wr)
+                                 for h in range(4))
+            ref_grads = gref.attention_grad_ref_window(q, k, v, g, 0.8, wl, wr)
+            for which in range(3):
+                base = [q, k, v][which]
+                fd = np.zeros_like(base)
+                for idx in np.ndindex(*base.shape):
+                    args = [q.copy(), k.copy(), v.copy()]
+                    args[which][idx] += h_
+                    up = loss(*args)
+                    args[which][idx] -= 2 * h_
+                    fd[idx] = (up - loss(*args)) / (2 * h_)
+                _close(ref_grads[which], fd, 2e-8, f"window driver H_kv={hkv} ({wl},{wr}) FD d{'QKV'[which]}")
+
+
+def pin_window_magnitudes():
+    """The window error-bound magnitudes: equal to the causal / unmasked ones
+    for the windows (-1, 0) and (-1, -1); closed forms for the window (0, 0)
+    (each row sees only its own key, P = I) and for two keys under (1, 0)
+    (row 0 sees key 0, row 1 sees keys 0 and 1 with P_10 = 1/(1+e^(S11-S10)));
+    and they bound the window gradients."""
+    rng = _rng(13)
+    n, d = 9, 4
+    q, k, v, g = (rng.normal(size=(n, d)) for _ in range(4))
+    for (wl, wr), causal in (((-1, 0), True), ((-1, -1), False)):
+        for a, b_ in zip(gref.grad_magnitudes_head_window(q, k, v, g, 0.5, wl, wr),
+                         gref.grad_magnitudes_head(q, k, v, g, 0.5, causal)):
+            _close(a, b_, 1e-13, f"magnitudes ({wl},{wr}) vs causal={causal}")
+    mq, mk, mv = gref.grad_magnitudes_head_window(q, k, v, g, 0.5, 0, 0)
+    ds = np.abs(np.einsum("id,id->i", g, v)) + np.einsum("id,id->i", np.abs(g), np.abs(v))
+    _close(mv, np.abs(g), 1e-14, "(0,0) mV = |dO|")
+    _close(mq, 0.5 * ds[:, None] * np.abs(k), 1e-13, "(0,0) mQ")
+    _close(mk, 0.5 * ds[:, None] * np.abs(q), 1e-13, "(0,0) mK")
+    q2, k2, v2, g2 = q[:2], k[:2], v[:2], g[:2]
+    s10, s11 = 0.5 * float(q2[1] @ k2[0]), 0.5 * float(q2[1] @ k2[1])
+    p10 = 1.0 / (1.0 + math.exp(s11 - s10))
+    _, _, mv2 = gref.grad_magnitudes_head_window(q2, k2, v2, g2, 0.5, 1, 0)
+    _close(mv2[0], np.abs(g2[0]) + p10 * np.abs(g2[1]), 1e-14, "(1,0) two keys: mV_0")
+    _close(mv2[1], (1.0 - p10) * np.abs(g2[1]), 1e-14, "(1,0) two keys: mV_1")
+    for wl, wr in ((2, 0), (1, 3), (-1, 1)):
+        grads = gref.attention_grad_head_window(q, k, v, g, 0.5, wl, wr)
+        mags = gref.grad_magnitudes_head_window(q, k, v, g, 0.5, wl, wr)
+        for name, gr, mg in zip("QKV", grads, mags):
+            assert np.all(np.abs(gr) <= mg * (1 + 1e-12) + 1e-300), f"({wl},{wr}) |d{name}| exceeds its magnitude"
+
+
 GRAD_PINS = [
     pin_window_grad_finite_differences,
+    pin_window_grad_driver_grouped_heads,
+    pin_window_magnitudes,
     pin_gqa_grad_finite_differences,
     pin_grad_finite_differences,
     pin_grad_single_key,

@@ -376,6 +376,28 @@ def pin_window_special_cases():
         _close(lse, lf, 1e-14, f"window ({wl},{wr}) vs full LSE")
 
 
+def pin_window_driver_grouped_heads():
+    """The [B, H] sliding-window driver: 6 query heads on 3 key/value heads
+    (query head h reads key/value head 0, 0, 1, 1, 2, 2) and on 1, two
+    sequences, windows that differ on the two sides.  Every (b, h) must equal
+    the loop-evaluated window attention on the key/value head it reads."""
+    rng = _rng(33)
+    B, H, n, d = 2, 6, 6, 3
+    q = rng.normal(size=(B, H, n, d))
+    for hkv, groups in ((3, [0, 0, 1, 1, 2, 2]), (1, [0] * 6)):
+        k, v = rng.normal(size=(B, hkv, n, d)), rng.normal(size=(B, hkv, n, 2))
+        for wl, wr in ((2, 0), (1, 3), (-1, 2), (3, -1)):
+            o, lse = ref.attention_ref_window(q, k, v, 0.7, wl, wr)
+            assert o.shape == (B, H, n, 2) and lse.shape == (B, H, n)
+            for b in range(B):
+                for h in range(H):
+                    g = groups[h]
+                    eo, el = _brute_force_window(q[b, h].tolist(), k[b, g].tolist(), v[b, g].tolist(), 0.7, wl, wr)
+                    tag = f"window driver H_kv={hkv} ({wl},{wr}) (b,h)=({b},{h})"
+                    _close(o[b, h], eo, 1e-12, tag + " O")
+                    _close(lse[b, h], el, 1e-12, tag + " LSE")
+
+
 def _same_with_inf(a, b, tol, what):
     """Equal -inf entries, the rest within tol."""
     a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
@@ -559,6 +581,7 @@ PINS = [
     pin_block_sparse_layouts,
     pin_window_brute_force,
     pin_window_special_cases,
+    pin_window_driver_grouped_heads,
     pin_gqa_head_groups,
     pin_brute_force,
     pin_hand_cases,

@@ -2,7 +2,12 @@
 
 * fa2_fp8_pack against the oracle's pack_fp8: the E4M3 codes and the fp32
   scales bit for bit (byte work), with and without rotation, d = 64 and 128,
-  ragged lengths, outliers.
+  ragged lengths, outliers.  Bit-exact codes need both sides to round the
+  rotated values identically, so this comparison also fixes the kernel to
+  the oracle's fp32 butterfly order (stage s pairs elements 2^s apart,
+  sum first, then difference).  The pages fix only the rotation as a
+  matrix; the order is this library's choice, and the oracle's pins check
+  the rotation against the matrix product (any order passes those).
 * fa2_fwd_fp8 against the oracle's attention of the dequantized codes,
   every element, at the bf16 forward bars (|O| <= 1e-2, |LSE| <= 1e-3 with
   fp32 O; plus half a bf16 ulp for bf16 O): the kernel's only differences

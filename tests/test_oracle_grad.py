@@ -54,6 +54,34 @@ def _gqa_last_head_wins(q, k, v, dout, scale, causal):
     return dq, dk, dv
 
 
+_orig_grad_window = gref.attention_grad_ref_window
+_orig_mag_window = gref.grad_magnitudes_head_window
+
+
+def _window_grad_driver(head_of, accumulate=True):
+    """A copy of the [B, H] window gradient driver: query head h reads
+    key/value head head_of(h, H, H_kv); accumulate=False stores a shared
+    head's gradient instead of adding it (the last query head wins)."""
+    def driver(q, k, v, dout, scale, wl, wr):
+        q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+        B, H = q.shape[:2]
+        Hkv = k.shape[1]
+        dq, dk, dv = np.empty_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                g = head_of(h, H, Hkv)
+                gq, gk, gv = gref.attention_grad_head_window(q[b, h], k[b, g], v[b, g], dout[b, h], scale, wl, wr)
+                dq[b, h] = gq
+                if accumulate:
+                    dk[b, g] += gk
+                    dv[b, g] += gv
+                else:
+                    dk[b, g] = gk
+                    dv[b, g] = gv
+        return dq, dk, dv
+    return driver
+
+
 MUTANTS = {
     "grad_v_untransposed_p": ("grad_v", lambda p, dout: p @ dout if p.shape[0] == dout.shape[0] else p.T @ dout + 1),
     "grad_v_sign": ("grad_v", lambda p, dout: -(p.T @ dout)),
@@ -68,6 +96,15 @@ MUTANTS = {
     "grad_k_untransposed_ds": ("grad_k", lambda ds, q, scale: float(scale) * (ds @ q)),
     "grad_k_sign": ("grad_k", lambda ds, q, scale: -float(scale) * (ds.T @ q)),
     "gqa_last_head_wins": ("attention_grad_ref_gqa", _gqa_last_head_wins),
+    "window_grad_driver_sides_swapped": ("attention_grad_ref_window", lambda q, k, v, g, s, wl, wr: _orig_grad_window(
+        q, k, v, g, s, wr, wl)),
+    "window_grad_driver_assigns": ("attention_grad_ref_window", _window_grad_driver(
+        lambda h, n_h, n_kv: h // (n_h // n_kv), accumulate=False)),
+    "window_grad_driver_heads_interleaved": ("attention_grad_ref_window", _window_grad_driver(
+        lambda h, n_h, n_kv: h % n_kv)),
+    "window_grad_driver_heads_ungrouped": ("attention_grad_ref_window", _window_grad_driver(lambda h, n_h, n_kv: h)),
+    "window_magnitudes_sides_swapped": ("grad_magnitudes_head_window", lambda q, k, v, g, s, wl, wr: _orig_mag_window(
+        q, k, v, g, s, wr, wl)),
 }
 
 

@@ -21,6 +21,24 @@ _orig_finalize = ref.finalize
 _orig_visible_window = ref.visible_window
 _orig_visible_bs = ref.visible_block_sparse
 _orig_gather = ref.gather_pages
+_orig_ref_window = ref.attention_ref_window
+
+
+def _window_driver_heads(head_of):
+    """A copy of the [B, H] window driver whose query head h reads the
+    key/value head head_of(h, H, H_kv)."""
+    def driver(q, k, v, scale, wl, wr):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H = q.shape[:2]
+        Hkv = k.shape[1]
+        o = np.empty(q.shape[:-1] + (v.shape[-1],))
+        lse = np.empty(q.shape[:-1])
+        for b in range(B):
+            for h in range(H):
+                g = head_of(h, H, Hkv)
+                o[b, h], lse[b, h] = ref.attention_head_window(q[b, h], k[b, g], v[b, g], scale, wl, wr)
+        return o, lse
+    return driver
 
 
 def _stats_no_shift(s, mask, v):
@@ -96,6 +114,11 @@ MUTANTS = {
     "decode_causal_from_start": ("visible_decode", lambda n, L: np.arange(L)[None, :] <= np.arange(n)[:, None]),
     "decode_sees_all_keys": ("visible_decode", lambda n, L: np.ones((n, L), dtype=bool)),
     "decode_excludes_own_key": ("visible_decode", lambda n, L: np.arange(L)[None, :] < (L - n + np.arange(n))[:, None]),
+    "window_driver_sides_swapped": ("attention_ref_window", lambda q, k, v, scale, wl, wr: _orig_ref_window(
+        q, k, v, scale, wr, wl)),
+    "window_driver_heads_ungrouped": ("attention_ref_window", _window_driver_heads(lambda h, n_h, n_kv: h)),
+    "window_driver_heads_interleaved": ("attention_ref_window", _window_driver_heads(lambda h, n_h, n_kv: h % n_kv)),
+    "window_driver_heads_clamped": ("attention_ref_window", _window_driver_heads(lambda h, n_h, n_kv: min(h, n_kv - 1))),
 }
 
 
