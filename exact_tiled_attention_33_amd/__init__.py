@@ -462,6 +462,35 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported dtype {dt} (bf16 or fp32)")
 
 
+def _check_buffer(t, name, shape, dtype, device):
+    """A buffer the kernels read or write through its raw address: it must be
+    a contiguous device tensor on ``device`` with exactly this shape and
+    dtype.  (A host tensor, a tensor on another device or a shorter one would
+    hand the kernel an address it cannot use; the C ABI cannot tell.)"""
+    if not getattr(t, "is_cuda", False) or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _check_on_device(device, **tensors):
+    """Inputs read through raw addresses: contiguous device tensors on ``device``."""
+    for name, t in tensors.items():
+        if not getattr(t, "is_cuda", False) or t.device != device:
+            raise ValueError(f"{name} must be a device tensor on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(ws, name, min_bytes, device):
+    """A device workspace of at least ``min_bytes`` bytes on ``device``."""
+    if not getattr(ws, "is_cuda", False) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor on {device}")
+    if ws.numel() * ws.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {ws.numel() * ws.element_size()} bytes, {min_bytes} needed")
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=None,
             out=None, lse=None, stream=None, window=None):
     """Attention forward on [B, H, N, d] device tensors; returns (o, lse).
@@ -481,10 +510,9 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
         raise ValueError(f"k, v heads must divide q's and the other dims match, got {q.shape}, {k.shape}")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not getattr(q, "is_cuda", False):
         raise ValueError("q, k, v must be device tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_on_device(q.device, q=q, k=k, v=v)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -493,10 +521,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, o_dtype=N
         out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, N, d] tensor of o_dtype")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_buffer(out, "out", q.shape, o_dtype, q.device)
+    _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -530,11 +556,9 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         raise ValueError(f"k, v heads must divide q's and the other dims match, got {q.shape}, {k.shape}")
     if not (q.dtype == k.dtype == v.dtype == dout.dtype):
         raise TypeError("q, k, v and dout must share a dtype")
-    tensors = (q, k, v, o, lse, dout)
-    if not all(t.is_cuda for t in tensors):
+    if not getattr(q, "is_cuda", False):
         raise ValueError("all tensors must be device tensors")
-    if not all(t.is_contiguous() for t in tensors):
-        raise ValueError("all tensors must be contiguous")
+    _check_on_device(q.device, q=q, k=k, v=v, o=o, lse=lse, dout=dout)
     B, H, N, d = q.shape
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, N] tensor")
@@ -543,12 +567,12 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer(delta, "delta", (B, H, N), torch.float32, q.device)
     outs = []
-    for t, shape in ((dq, q.shape), (dk, k.shape), (dv, k.shape)):
+    for t, name, shape in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
         if t is None:
             t = torch.empty(shape, dtype=grad_dtype, device=q.device)
-        if t.shape != shape or t.dtype != grad_dtype or not t.is_contiguous():
-            raise ValueError("dq (q's shape), dk, dv (k's shape) must be contiguous tensors of grad_dtype")
+        _check_buffer(t, name, shape, grad_dtype, q.device)
         outs.append(t)
     dq, dk, dv = outs
     if stream is None:
@@ -589,10 +613,9 @@ def forward_split(q, k, v, plan: SplitPlan, causal: bool = False, scale: float |
 
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not getattr(q, "is_cuda", False):
         raise ValueError("q, k, v must be device tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_on_device(q.device, q=q, k=k, v=v)
     B, H, N, d = q.shape
     wl, wr = (-1, 0 if causal else -1) if window is None else window
     if plan.shape != (B, H, N, d) or plan.window != (wl, wr):
@@ -604,12 +627,12 @@ def forward_split(q, k, v, plan: SplitPlan, causal: bool = False, scale: float |
         out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, N, d] tensor of o_dtype")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_buffer(out, "out", q.shape, o_dtype, q.device)
+    _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if workspace is None and plan.workspace_bytes > 0:
         workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_workspace(workspace, "workspace", plan.workspace_bytes, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:
@@ -633,10 +656,9 @@ def forward_sparse(q, k, v, plan: SparsePlan, scale: float | None = None, o_dtyp
 
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not getattr(q, "is_cuda", False):
         raise ValueError("q, k, v must be device tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_on_device(q.device, q=q, k=k, v=v)
     B, H, N, d = q.shape
     if plan.N != N:
         raise ValueError(f"plan was built for N = {plan.N}, not {N}")
@@ -647,10 +669,8 @@ def forward_sparse(q, k, v, plan: SparsePlan, scale: float | None = None, o_dtyp
         out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, N, d] tensor of o_dtype")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_buffer(out, "out", q.shape, o_dtype, q.device)
+    _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -680,9 +700,10 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, max_context: int
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError(f"q must be [B, H, n_q, d], caches [n_pages, page_size, H_kv, d]; got {q.shape}, "
                          f"{k_cache.shape}, {v_cache.shape}")
-    for t in (q, k_cache, v_cache, page_table, context_lens):
-        if not (t.is_cuda and t.is_contiguous()):
-            raise ValueError("all tensors must be contiguous device tensors")
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("all tensors must be contiguous device tensors")
+    _check_on_device(q.device, q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
+                     context_lens=context_lens)
     if page_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise TypeError("page_table and context_lens must be int32")
     B, H, n_q, d = q.shape
@@ -696,14 +717,13 @@ def decode_paged(q, k_cache, v_cache, page_table, context_lens, max_context: int
     split_keys, ws_bytes = fa2_decode_paged_workspace(B, H, H_kv, n_q, d, max_context, split_keys, units)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, "workspace", ws_bytes, q.device)
     if out is None:
         out = torch.empty((B, H, n_q, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != o_dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, H, n_q, d] tensor of o_dtype")
-    if lse.shape != (B, H, n_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, n_q] tensor")
+    _check_buffer(out, "out", q.shape, o_dtype, q.device)
+    _check_buffer(lse, "lse", (B, H, n_q), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -731,6 +751,7 @@ def fp8_pack(x, signs=None, stream=None, workspace=None):
     ws_bytes = fa2_fp8_pack_workspace(B, H, N)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _check_workspace(workspace, "workspace", ws_bytes, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -751,6 +772,9 @@ def forward_fp8(q, k, v, signs=None, causal: bool = False, scale: float | None =
 
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError(f"q must be [B, H, N, d] and k, v [B, H_kv, N, d], got {q.shape}, {k.shape}, {v.shape}")
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("q, k, v must be device tensors")
+    _check_on_device(q.device, q=q, k=k, v=v)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -759,11 +783,17 @@ def forward_fp8(q, k, v, signs=None, causal: bool = False, scale: float | None =
         k8, ks = fp8_pack(k, signs, stream)
     else:
         q8, qs, k8, ks = packed
+    _check_buffer(q8, "q8", q.shape, torch.uint8, q.device)
+    _check_buffer(qs, "q_scale", (B, H), torch.float32, q.device)
+    _check_buffer(k8, "k8", k.shape, torch.uint8, q.device)
+    _check_buffer(ks, "k_scale", tuple(k.shape[:2]), torch.float32, q.device)
     o_dtype = torch.float32 if o_dtype is None else o_dtype
     if out is None:
         out = torch.empty((B, H, N, d), dtype=o_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer(out, "out", q.shape, o_dtype, q.device)
+    _check_buffer(lse, "lse", (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

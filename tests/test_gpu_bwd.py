@@ -195,3 +195,25 @@ def test_long_causal_workload():
     for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
         _check_head([x[b, h] for x in got], Q[b, h], K[b, h], V[b, h], G[b, h], w.scale, w.causal,
                     f"long_causal head ({b},{h})")
+
+
+def test_buffer_rejections_on_gpu():
+    """Caller-supplied delta, dq, dk, dv that are host tensors, wrongly sized
+    or wrongly typed raise ValueError before any launch."""
+    q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV)
+    o, lse = fa2.forward(q, q, q)
+    g = torch.zeros(1, 2, 64, 128, dtype=torch.float32, device=DEV)
+    print("[case] bwd buffer rejections", flush=True)
+    bad = [
+        dict(delta=torch.empty(1, 2, 64)),                                    # host
+        dict(delta=torch.empty(1, 2, 63, device=DEV)),                        # short
+        dict(delta=torch.empty(1, 2, 64, dtype=torch.bfloat16, device=DEV)),  # dtype
+        dict(delta=torch.empty(1, 2, 128, device=DEV)[:, :, ::2]),            # strided
+        dict(dq=torch.empty(1, 2, 64, 128)),                                  # host
+        dict(dk=torch.empty(1, 2, 64, 64, device=DEV)),                       # shape
+        dict(dv=torch.empty(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            fa2.backward(q, q, q, o, lse, g, **kw)
+    torch.cuda.synchronize()

@@ -243,6 +243,19 @@ def test_error_status_on_gpu():
     assert e.value.status == fa2.FA2_ERR_UNSUPPORTED
 
 
+def test_buffer_rejections_on_gpu():
+    """A host or wrongly sized out/lse raises ValueError before any launch."""
+    q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV)
+    print("[case] forward buffer rejections", flush=True)
+    for kw in (dict(out=torch.empty(1, 2, 64, 128)), dict(lse=torch.empty(1, 2, 64)),
+               dict(lse=torch.empty(1, 2, 32, device=DEV)),
+               dict(out=torch.empty(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV))):
+        with pytest.raises(ValueError):
+            fa2.forward(q, q, q, **kw)
+    with pytest.raises(ValueError):
+        fa2.forward(q, q.cpu(), q)
+
+
 # --- LDS-poison debug mode ------------------------------------------------------
 # With FA2_DEBUG_POISON set, the bf16 kernel fills every LDS ring slot with
 # NaN before a K/V tile is copied into it.  If a wave read a slot before its
