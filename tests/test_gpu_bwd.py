@@ -202,7 +202,7 @@ def test_buffer_rejections_on_gpu():
     or wrongly typed raise ValueError before any launch."""
     q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV)
     o, lse = fa2.forward(q, q, q)
-    g = torch.zeros(1, 2, 64, 128, dtype=torch.float32, device=DEV)
+    g = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV)
     print("[case] bwd buffer rejections", flush=True)
     bad = [
         dict(delta=torch.empty(1, 2, 64)),                                    # host

@@ -106,7 +106,7 @@ def test_decode_rejections_on_gpu():
     ctx = torch.tensor([100], dtype=torch.int32, device=DEV)
     kd, vd, td = kc.to(DEV), vc.to(DEV), table.to(DEV)
     small = torch.empty(16, dtype=torch.uint8, device=DEV)
-    with pytest.raises(fa2.Fa2Error):
+    with pytest.raises(ValueError):
         fa2.decode_paged(q, kd, vd, td, ctx, max_context=100, workspace=small)
     kc32, vc32, t32 = workloads.make_paged_cache([100], 2, 128, 32, seed=80)
     with pytest.raises(fa2.Fa2Error) as e:
