@@ -25,6 +25,8 @@ Raw entry points (same names and argument order as the C ABI):
     fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages,
         context_lens, max_context, page_size, n_pages, split_keys, workspace, workspace_bytes,
         stream, in_dtype, o_dtype) -> int
+    fa2_decode_paged_noalloc(... the same without workspace, workspace_bytes ...) -> int
+        (partials in a static per-device scratch of FA2_DECODE_SCRATCH_BYTES)
     fa2_fp8_pack_workspace(B, H, N) -> bytes
     fa2_fp8_pack(x, B, H, N, d, signs, codes, scales, workspace, workspace_bytes, stream) -> int
     fa2_fwd_fp8(q8, q_scale, k8, k_scale, v, o, lse, B, H, H_kv, N, d, causal, scale, stream, o_dtype) -> int
@@ -51,11 +53,11 @@ from pathlib import Path
 __all__ = [
     "F32", "BF16",
     "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
-    "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
+    "FA2_ERR_SCRATCH", "FA2_DECODE_SCRATCH_BYTES", "Fa2Error", "library_path", "load", "fa2_fwd", "fa2_plan", "fa2_strerror", "fa2_version",
     "fa2_bwd", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_window", "fa2_bwd_window", "forward", "backward",
     "fa2_split_plan", "fa2_fwd_split", "SplitPlan", "split_plan", "forward_split",
     "fa2_sparse_plan", "fa2_fwd_sparse", "SparsePlan", "forward_sparse",
-    "fa2_decode_paged_workspace", "fa2_decode_paged", "decode_paged",
+    "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_decode_paged_noalloc", "decode_paged",
     "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fp8_pack", "forward_fp8",
     "EXPORTED_SYMBOLS",
 ]
@@ -68,11 +70,14 @@ FA2_ERR_INVALID_ARG = -1
 FA2_ERR_UNSUPPORTED = -2
 FA2_ERR_NO_DEVICE = -3
 FA2_ERR_LAUNCH = -4
+FA2_ERR_SCRATCH = -5
+
+FA2_DECODE_SCRATCH_BYTES = 16 << 20
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
                     "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_sparse_plan",
-                    "fa2_fwd_sparse", "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_fp8_pack_workspace",
-                    "fa2_fp8_pack", "fa2_fwd_fp8", "fa2_strerror", "fa2_version")
+                    "fa2_fwd_sparse", "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_decode_paged_noalloc",
+                    "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -267,6 +272,13 @@ def load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
     ]
+    lib.fa2_decode_paged_noalloc.restype = ctypes.c_int
+    lib.fa2_decode_paged_noalloc.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+    ]
     lib.fa2_fp8_pack_workspace.restype = ctypes.c_int
     lib.fa2_fp8_pack_workspace.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
     lib.fa2_fp8_pack.restype = ctypes.c_int
@@ -413,6 +425,15 @@ def fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, pag
     return int(load().fa2_decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, float(scale), page_table,
                                        max_pages, context_lens, max_context, page_size, n_pages, split_keys,
                                        workspace, int(workspace_bytes), stream, in_dtype, o_dtype))
+
+
+def fa2_decode_paged_noalloc(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages,
+                             context_lens, max_context, page_size, n_pages, split_keys, stream, in_dtype,
+                             o_dtype) -> int:
+    """Raw C call: pointers and sizes as Python ints; returns the status code."""
+    return int(load().fa2_decode_paged_noalloc(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, float(scale),
+                                               page_table, max_pages, context_lens, max_context, page_size,
+                                               n_pages, split_keys, stream, in_dtype, o_dtype))
 
 
 def fa2_fp8_pack_workspace(B, H, N) -> int:

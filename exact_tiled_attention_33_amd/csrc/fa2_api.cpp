@@ -196,6 +196,7 @@ const char* fa2_strerror(int status) {
     case FA2_ERR_UNSUPPORTED: return "unsupported configuration (forward: head dim 64 or 128; backward: bf16 inputs, head dim 128)";
     case FA2_ERR_NO_DEVICE: return "no HIP device available";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
+    case FA2_ERR_SCRATCH: return "the call needs more than the static scratch of a no-alloc entry point";
     default: return "unknown status";
   }
 }
@@ -477,12 +478,17 @@ int fa2_decode_paged_workspace(int B, int H, int H_kv, int n_q, int d, int max_c
   return FA2_OK;
 }
 
-int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
-                     int H_kv, int n_q, int d, float scale, const int* page_table, int max_pages,
-                     const int* context_lens, int max_context, int page_size, int n_pages, int split_keys,
-                     void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype) {
-  if (!q || !k_cache || !v_cache || !o || !lse || !page_table || !context_lens || !workspace)
-    return FA2_ERR_INVALID_ARG;
+namespace {
+
+// fa2_decode_paged and fa2_decode_paged_noalloc: with from_scratch the
+// partials go to the static per-device scratch instead of `workspace`.
+int decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+                 int H_kv, int n_q, int d, float scale, const int* page_table, int max_pages,
+                 const int* context_lens, int max_context, int page_size, int n_pages, int split_keys,
+                 void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype,
+                 bool from_scratch) {
+  if (!q || !k_cache || !v_cache || !o || !lse || !page_table || !context_lens) return FA2_ERR_INVALID_ARG;
+  if (!from_scratch && !workspace) return FA2_ERR_INVALID_ARG;
   if (!is_dtype(in_dtype) || !is_dtype(o_dtype)) return FA2_ERR_INVALID_ARG;
   if (max_pages < 1 || n_pages < 1 || page_size < 1 || split_keys < 1) return FA2_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_INVALID_ARG;
@@ -495,9 +501,13 @@ int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, vo
   if (page_size % bc != 0) return FA2_ERR_UNSUPPORTED;  // a key tile must lie in one page
   if ((long double)n_pages * page_size * H_kv * d > (long double)(1LL << 60)) return FA2_ERR_INVALID_ARG;
   if ((long double)max_pages * page_size > 2147483647.0L) return FA2_ERR_INVALID_ARG;
-  if (workspace_bytes < need) return FA2_ERR_INVALID_ARG;
+  if (from_scratch) {
+    if (need > FA2_DECODE_SCRATCH_BYTES) return FA2_ERR_SCRATCH;
+  } else if (workspace_bytes < need) {
+    return FA2_ERR_INVALID_ARG;
+  }
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
-      !aligned(workspace, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4))
+      (!from_scratch && !aligned(workspace, 16)) || !aligned(page_table, 4) || !aligned(context_lens, 4))
     return FA2_ERR_INVALID_ARG;
   const size_t rows = (size_t)B * H * n_q;
   const size_t q_bytes = rows * d * 2;
@@ -506,19 +516,22 @@ int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, vo
   const size_t cache_bytes = (size_t)n_pages * page_size * H_kv * d * 2;
   const size_t table_bytes = (size_t)B * max_pages * sizeof(int);
   const size_t lens_bytes = (size_t)B * sizeof(int);
-  // written buffers against everything else
+  // written buffers against everything else (the static scratch is its own
+  // allocation and cannot overlap a caller's buffer)
+  const int n_out = from_scratch ? 2 : 3;
   const void* outs[3] = {o, lse, workspace};
   const size_t out_sz[3] = {o_bytes, lse_bytes, need};
   const void* ins[6] = {q, k_cache, v_cache, page_table, context_lens, nullptr};
   const size_t in_sz[6] = {q_bytes, cache_bytes, cache_bytes, table_bytes, lens_bytes, 0};
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < n_out; ++i) {
     for (int j = 0; j < 5; ++j)
       if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA2_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 3; ++j)
+    for (int j = i + 1; j < n_out; ++j)
       if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA2_ERR_INVALID_ARG;
   }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;
+  if (from_scratch && fa2::decode_scratch(&workspace) != hipSuccess) return FA2_ERR_LAUNCH;
 
   fa2::FwdArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse;
@@ -543,6 +556,25 @@ int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, vo
   a.stream = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = fa2::launch_decode_paged(a);
   return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+                     int H_kv, int n_q, int d, float scale, const int* page_table, int max_pages,
+                     const int* context_lens, int max_context, int page_size, int n_pages, int split_keys,
+                     void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype) {
+  return decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages, context_lens,
+                      max_context, page_size, n_pages, split_keys, workspace, workspace_bytes, stream, in_dtype,
+                      o_dtype, false);
+}
+
+int fa2_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B,
+                             int H, int H_kv, int n_q, int d, float scale, const int* page_table, int max_pages,
+                             const int* context_lens, int max_context, int page_size, int n_pages, int split_keys,
+                             void* stream, int in_dtype, int o_dtype) {
+  return decode_paged(q, k_cache, v_cache, o, lse, B, H, H_kv, n_q, d, scale, page_table, max_pages, context_lens,
+                      max_context, page_size, n_pages, split_keys, nullptr, 0, stream, in_dtype, o_dtype, true);
 }
 
 int fa2_fp8_pack_workspace(int B, int H, int N, size_t* workspace_bytes) {

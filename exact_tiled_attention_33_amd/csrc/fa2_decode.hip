@@ -22,9 +22,43 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
+#include "fa2.h"
 #include "fa2_launch.h"
 
+// Partial results of fa2_decode_paged_noalloc.  The runtime gives every
+// device its own copy, kept until the process ends.  In host code this name
+// stands for the variable, not a device address: only the per-device address
+// that decode_scratch() looks up may be handed to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[FA2_DECODE_SCRATCH_BYTES];
+
 namespace fa2 {
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> by_device[kMaxDevices];
+  static std::mutex lookup;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = by_device[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> g(lookup);
+    p = by_device[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      by_device[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

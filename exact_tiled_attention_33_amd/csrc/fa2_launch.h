@@ -145,6 +145,9 @@ hipError_t launch_split_merge(const FwdArgs& a);
 
 // Enqueue paged decoding: the chunk kernel, then the merge of its partials.
 hipError_t launch_decode_paged(const FwdArgs& a);
+// Device address of the static decode scratch (FA2_DECODE_SCRATCH_BYTES) on
+// the current device, looked up once per device.
+hipError_t decode_scratch(void** ptr);
 
 // The chunk kernel of paged decoding with one wavefront per (chunk, group)
 // (fa2_decode.hip), for groups of at most 32 query rows.

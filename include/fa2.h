@@ -37,7 +37,10 @@
  *   - Arguments are validated before any HIP call; on error nothing is
  *     launched and a negative fa2_status is returned.  No output is printed
  *     and no exception crosses the ABI.
- *   - The library keeps no mutable global state and is re-entrant.
+ *   - The library keeps no mutable global state and is re-entrant, with one
+ *     exception: fa2_decode_paged_noalloc writes its partial results to a
+ *     static buffer of FA2_DECODE_SCRATCH_BYTES per device, shared by all of
+ *     its calls on that device.
  */
 #ifndef FA2_H
 #define FA2_H
@@ -60,8 +63,12 @@ typedef enum fa2_status {
   FA2_ERR_INVALID_ARG = -1, /* null or misaligned pointer, bad size, bad scale, bad dtype code */
   FA2_ERR_UNSUPPORTED = -2, /* valid arguments outside what the kernels implement (head dim, dtype pair) */
   FA2_ERR_NO_DEVICE = -3,   /* no usable HIP device is current */
-  FA2_ERR_LAUNCH = -4       /* the kernel launch was rejected by the runtime */
+  FA2_ERR_LAUNCH = -4,      /* the kernel launch was rejected by the runtime */
+  FA2_ERR_SCRATCH = -5      /* the call needs more than FA2_DECODE_SCRATCH_BYTES of static scratch */
 } fa2_status;
+
+/* Size of the static per-device scratch of fa2_decode_paged_noalloc (16 MiB). */
+#define FA2_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
 
 /*
  * fa2_fwd -- attention forward: O and the per-row logsumexp.
@@ -465,6 +472,32 @@ int fa2_decode_paged(const void* q, const void* k_cache, const void* v_cache, vo
                      const int* page_table, int max_pages, const int* context_lens, int max_context,
                      int page_size, int n_pages, int split_keys,
                      void* workspace, size_t workspace_bytes, void* stream, int in_dtype, int o_dtype);
+
+/*
+ * fa2_decode_paged_noalloc -- fa2_decode_paged without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid it).  It allocates nothing: the partial results go to a static
+ * device buffer of FA2_DECODE_SCRATCH_BYTES that each device the library
+ * runs on holds until the process ends (its address is looked up once per
+ * device, on the first call with that device current).
+ *
+ * Arguments, kernels and results are those of fa2_decode_paged with the
+ * same split_keys (o and lse are bitwise the same).  A call whose
+ * fa2_decode_paged_workspace bytes exceed FA2_DECODE_SCRATCH_BYTES returns
+ * FA2_ERR_SCRATCH before any HIP call (use fa2_decode_paged with a
+ * workspace, or a larger split_keys).  No part of the scratch needs to
+ * start at zero: each call writes every partial it reads.
+ *
+ * All calls on one device share the scratch: two calls whose kernels
+ * overlap in time on the same device (on different streams, or from
+ * different host threads without ordering) race and give wrong results.
+ * Calls ordered on one stream are safe.
+ */
+int fa2_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                             int B, int H, int H_kv, int n_q, int d, float scale,
+                             const int* page_table, int max_pages, const int* context_lens, int max_context,
+                             int page_size, int n_pages, int split_keys, void* stream, int in_dtype, int o_dtype);
 
 /*
  * fa2_fp8_pack_workspace -- workspace bytes of fa2_fp8_pack for [B, H, N, .]

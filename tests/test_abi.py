@@ -46,9 +46,12 @@ def test_version_matches_header():
 
 def test_status_codes_match_header():
     text = HEADER.read_text()
-    for name in ("FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH"):
+    for name in ("FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_NO_DEVICE", "FA2_ERR_LAUNCH",
+                 "FA2_ERR_SCRATCH"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert int(m.group(1)) == getattr(fa2, name), name
+    m = re.search(r"#define FA2_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert int(m.group(1)) << int(m.group(2)) == fa2.FA2_DECODE_SCRATCH_BYTES
     for name in ("F32", "BF16"):
         m = re.search(rf"\bFA2_{name}\s*=\s*(\d+)", text)
         assert int(m.group(1)) == getattr(fa2, name)
@@ -56,7 +59,7 @@ def test_status_codes_match_header():
 
 def test_strerror():
     for st in (fa2.FA2_OK, fa2.FA2_ERR_INVALID_ARG, fa2.FA2_ERR_UNSUPPORTED, fa2.FA2_ERR_NO_DEVICE,
-               fa2.FA2_ERR_LAUNCH, 12345):
+               fa2.FA2_ERR_LAUNCH, fa2.FA2_ERR_SCRATCH, 12345):
         assert isinstance(fa2.fa2_strerror(st), str) and fa2.fa2_strerror(st)
     assert fa2.fa2_strerror(12345) == "unknown status"
 

@@ -86,3 +86,48 @@ def test_decode_validation(over, status):
 def test_decode_no_device_status_on_cpu_only_host():
     assert _call() == fa2.FA2_ERR_NO_DEVICE
     assert _call(n_q=4, split=64, page=256, o_dtype=fa2.BF16) == fa2.FA2_ERR_NO_DEVICE
+
+
+# --- fa2_decode_paged_noalloc: the same checks, no workspace argument -------
+
+def _call_noalloc(**over):
+    a = dict(GOOD, **over)
+    return fa2.fa2_decode_paged_noalloc(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                                        a["n_q"], a["d"], a["scale"], a["pt"], a["max_pages"], a["cl"],
+                                        a["max_ctx"], a["page"], a["n_pages"], a["split"], a["stream"],
+                                        a["in_dtype"], a["o_dtype"])
+
+
+@pytest.mark.parametrize("over, status", [
+    (dict(q=0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(pt=0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(split=0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(split=100), fa2.FA2_ERR_INVALID_ARG),
+    (dict(page=96), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(in_dtype=fa2.F32), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(o=KC + 64), fa2.FA2_ERR_INVALID_ARG),
+    (dict(lse=CL), fa2.FA2_ERR_INVALID_ARG),
+    (dict(pt=PT + 2), fa2.FA2_ERR_INVALID_ARG),
+])
+def test_noalloc_validation(over, status):
+    assert _call_noalloc(**over) == status
+
+
+# 64 sequences x 32 query heads, one new token, d = 128: 2048 rows of
+# 128*4 + 8 bytes per 64-key chunk; 16 chunks need 17,039,360 bytes.
+BIG = dict(B=64, H=32, Hkv=8, n_q=1, d=128, split=64, max_pages=16, page=64, n_pages=1024)
+
+
+def test_noalloc_rejects_more_than_the_scratch():
+    need = fa2.fa2_decode_paged_workspace(64, 32, 8, 1, 128, 1024, 64, 0)[1]
+    assert need == 16 * 2048 * (128 * 4 + 8) > fa2.FA2_DECODE_SCRATCH_BYTES
+    assert _call_noalloc(max_ctx=1024, **BIG) == fa2.FA2_ERR_SCRATCH
+    assert "scratch" in fa2.fa2_strerror(fa2.FA2_ERR_SCRATCH)
+
+
+@pytest.mark.skipif(_gpu_present(), reason="valid fake pointers would launch on a real GPU")
+def test_noalloc_no_device_status_on_cpu_only_host():
+    assert _call_noalloc() == fa2.FA2_ERR_NO_DEVICE
+    # 15 chunks (15,974,400 bytes) fit in the scratch
+    assert fa2.fa2_decode_paged_workspace(64, 32, 8, 1, 128, 960, 64, 0)[1] <= fa2.FA2_DECODE_SCRATCH_BYTES
+    assert _call_noalloc(max_ctx=960, **BIG) == fa2.FA2_ERR_NO_DEVICE
