@@ -60,6 +60,7 @@
 
 #include "fa2_launch.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -983,17 +984,44 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // first MFMAs) into the slots of K_j and V_{j-2}, which nobody reads after
 // the barrier that starts tile j; the barrier at the end of tile j, after
 // each wavefront's wait for its own copies, publishes them.
+//
+// A workgroup may own several (query tile, batch*head) items in turn
+// (`sched`): 0 = one item, blockIdx.x; 1 = items g, g + G, g + 2G, ... (G
+// workgroups) for grids of equal items larger than the chip holds at once,
+// so that the cost of starting an item (its first loads, the store of its
+// O) overlaps other work instead of hitting every compute unit at once
+// (Saraf, section 2.3: keep every unit busy); 2 = a snake over the
+// heaviest-first order (items g and 2G-1-g, then 2G+g, ...), which pairs
+// long causal items with short ones into equal loads when there are at
+// most two per workgroup slot.  The last P V product of an item reads no
+// K, so its stream copies the next item's first two K tiles into the K ring
+// and loads the next item's Q rows: those loads are in flight while the
+// item finishes and stores O, and the next item waits for them alone.
+//
+// O leaves through LDS (a quarter of the V ring per wavefront): each store
+// instruction then writes whole rows of O instead of 32-byte pieces of 32
+// rows, and exactly 1 KiB per instruction, so a wavefront issues a fixed
+// number of stores per item.
 constexpr int kRing2 = 2;               // K (and V) tiles resident per ring
 constexpr int kW4 = kFwdWaves;          // wavefronts per workgroup (one per SIMD)
 constexpr int kBr4 = kFwdBlockRows;     // query rows per workgroup
 constexpr int kThreads4 = kW4 * 64;
 constexpr int kAheadIL = 3;             // LDS operand reads in flight ahead of the MFMAs
 static_assert(kBr4 == kW4 * kRows, "each wavefront owns 32 query rows");
-template <int D, bool MASKED, bool OUT_BF16>
+
+// s_waitcnt with a compile-time vector-memory count of up to 63 (gfx9: the
+// count's low 4 bits in bits 3:0, its high 2 bits in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int D, bool MASKED, bool OUT_BF16, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads4, kThreads4), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                void* __restrict__ o, float* __restrict__ lse, int BH, int N, int T, float c, int poison, int group,
-               int wl, int wr) {
+               int wl, int wr, int n_items, int sched) {
   using G = Geo<D, false>;
   __shared__ __attribute__((aligned(1024))) char smem[kRing2 * (G::kTileK + G::kTileV)];
   char* const lds_k = smem;
@@ -1005,57 +1033,80 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // Grid: workgroup -> (batch*head, query tile); causal and window tiles are
-  // issued heaviest (latest rows) first; without a mask and with heads in
-  // multiples of 8, consecutive workgroups of one XCD (blockIdx.x = x + 8r
-  // goes to XCD x) take the T tiles of one head, so its K and V are fetched
+  // Item -> (batch*head, query tile): causal and window tiles in heaviest
+  // (latest rows) first order; without a mask and with heads in multiples of
+  // 8, items x + 8r (whose workgroups all run on XCD x when the grid is a
+  // multiple of 8) take the T tiles of one head, so its K and V are fetched
   // into that XCD's L2 once.
   const bool xcd_major = !MASKED && (BH & 7) == 0;
-  const int xcd_r = (int)(blockIdx.x >> 3);
-  const int bh = xcd_major ? (xcd_r / T) * 8 + (int)(blockIdx.x & 7) : (int)(blockIdx.x % BH);
-  const int t = xcd_major ? xcd_r % T : (MASKED ? (T - 1 - (int)(blockIdx.x / BH)) : (int)(blockIdx.x / BH));
+  const int n_wg = (int)gridDim.x, wg = (int)blockIdx.x;
+  auto item_of = [&](int r) __attribute__((always_inline)) {
+    const int i = (!PERSIST || sched == 0) ? (r == 0 ? wg : n_items)
+                : sched == 1 ? wg + r * n_wg
+                             : r * n_wg + ((r & 1) ? n_wg - 1 - wg : wg);
+    return i < n_items ? i : -1;
+  };
   const int n_keys = N;
-  const long long head = (long long)bh * N * D;
-  const long long kv_head = (long long)(bh / group) * N * D;
-  const char* const kh = (const char*)(k + kv_head);
-  const char* const vh = (const char*)(v + kv_head);
-
-  const int q0 = t * kBr4;
-  const int qw = q0 + 32 * wave;
-  const int qrow = qw + l32;
-
-  // Q rows of the wavefront as MFMA B operands, held for the whole key loop;
-  // rows past N read as zeros.
-  bf16x8 qf[G::kKSteps];
-  {
-    const int rows = max(0, min(kRows, N - qw));
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head + (long long)min(qw, N) * D, rows * D * 2);
-#pragma unroll
-    for (int s = 0; s < G::kKSteps; ++s) qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (l32 * D + 16 * s + 8 * half) * 2));
-  }
-
+  const int nk = (n_keys + kBc - 1) / kBc;
   // Key tiles j_lo .. j_lo + n_tiles - 1 hold a key some row of the
   // workgroup sees (key j visible to query i iff i - wl <= j <= i + wr, a
   // negative bound meaning no limit); this wavefront's rows see every key of
   // tiles jf_lo .. jf_hi - 1, which therefore need no mask.
-  const int nk = (n_keys + kBc - 1) / kBc;
-  int j_lo = 0, n_tiles = nk, jf_lo = 0, jf_hi = n_keys / kBc;
-  if (MASKED) {
-    const int q_last = min(q0 + kBr4, N) - 1;
-    const int w_last = min(qw + kRows, N) - 1;
-    if (wl >= 0) {
-      j_lo = max(0, q0 - wl) / kBc;
-      jf_lo = (max(0, w_last - wl) + kBc - 1) / kBc;
+  struct Item { int bh, t, j_lo, n_tiles, jf_lo, jf_hi; };
+  auto geom = [&](int i) __attribute__((always_inline)) {
+    Item it;
+    it.bh = xcd_major ? ((i >> 3) / T) * 8 + (i & 7) : i % BH;
+    it.t = xcd_major ? (i >> 3) % T : (MASKED ? (T - 1 - i / BH) : i / BH);
+    const int q0 = it.t * kBr4, qw = q0 + 32 * wave;
+    it.j_lo = 0;
+    it.n_tiles = nk;
+    it.jf_lo = 0;
+    it.jf_hi = n_keys / kBc;
+    if (MASKED) {
+      const int q_last = min(q0 + kBr4, N) - 1;
+      const int w_last = min(qw + kRows, N) - 1;
+      if (wl >= 0) {
+        it.j_lo = max(0, q0 - wl) / kBc;
+        it.jf_lo = (max(0, w_last - wl) + kBc - 1) / kBc;
+      }
+      int j_hi = nk;
+      if (wr >= 0) {
+        j_hi = min(nk, (q_last + wr) / kBc + 1);
+        it.jf_hi = min(it.jf_hi, qw + wr - (kBc - 1) >= 0 ? (qw + wr - (kBc - 1)) / kBc + 1 : 0);
+      }
+      it.n_tiles = j_hi - it.j_lo;
     }
-    int j_hi = nk;
-    if (wr >= 0) {
-      j_hi = min(nk, (q_last + wr) / kBc + 1);
-      jf_hi = min(jf_hi, qw + wr - (kBc - 1) >= 0 ? (qw + wr - (kBc - 1)) / kBc + 1 : 0);
-    }
-    n_tiles = j_hi - j_lo;
-  }
-  const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
-  const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
+    return it;
+  };
+
+  int item = item_of(0);
+  if (item < 0) return;
+  Item cur = geom(item);
+  // the current item's addresses and row bounds (set by enter())
+  long long head = 0;
+  const char* kh = nullptr;
+  const char* vh = nullptr;
+  int qw = 0, qrow = 0, key_lo = 0, key_hi = 0;
+  auto enter = [&]() __attribute__((always_inline)) {
+    head = (long long)cur.bh * N * D;
+    const long long kv_head = (long long)(cur.bh / group) * N * D;
+    kh = (const char*)(k + kv_head);
+    vh = (const char*)(v + kv_head);
+    qw = cur.t * kBr4 + 32 * wave;
+    qrow = qw + l32;
+    key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
+    key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
+  };
+
+  // Q rows of the wavefront as MFMA B operands, held for an item's key loop;
+  // rows past N read as zeros.
+  bf16x8 qf[G::kKSteps];
+  auto load_q = [&](long long head_, int qw_) __attribute__((always_inline)) {
+    const int rows = max(0, min(kRows, N - qw_));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_ + (long long)min(qw_, N) * D, rows * D * 2);
+#pragma unroll
+    for (int s = 0; s < G::kKSteps; ++s) qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (l32 * D + 16 * s + 8 * half) * 2));
+  };
 
   // ---- copies: one instruction = 64 lanes x 16 bytes into 64 consecutive
   // 16-byte LDS slots; instruction i of a tile is issued by wavefront i % 4
@@ -1080,18 +1131,23 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   }
   const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
   const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
-  // this wavefront's instruction kk of key tile jt into ring slot `slot`.
-  // jt is clamped to the last tile (a copy past the end fetches it again
-  // into a slot nobody reads); rows past N come from row N-1 and are masked.
-  auto copy_k = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
-    const int key0 = (j_lo + min(jt, n_tiles - 1)) * kBc;
+  // this wavefront's instruction kk of key tile jt (of the item whose keys
+  // start at kbase, with tiles j_lo_ .. j_lo_ + n_tiles_ - 1) into ring slot
+  // `slot`.  jt is clamped to the last tile (a copy past the end fetches it
+  // again into a slot nobody reads); rows past N come from row N-1 and are
+  // masked.
+  auto copy_k_of = [&](const char* kbase, int j_lo_, int n_tiles_, int jt, int slot, int kk) __attribute__((always_inline)) {
+    const int key0 = (j_lo_ + min(jt, n_tiles_ - 1)) * kBc;
     const int rows = min(kBc, n_keys - key0);
-    const unsigned long long gsrc = uniform_addr(kh + (long long)key0 * G::kRowBytes);
+    const unsigned long long gsrc = uniform_addr(kbase + (long long)key0 * G::kRowBytes);
     const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
     copy16_to_lds(gsrc, min(voff_k[kk], lim), lds_k0 + slot * G::kTileK + kk * kW4 * 1024);
   };
+  auto copy_k = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
+    copy_k_of(kh, cur.j_lo, cur.n_tiles, jt, slot, kk);
+  };
   auto copy_v = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
-    const int key0 = (j_lo + min(jt, n_tiles - 1)) * kBc;
+    const int key0 = (cur.j_lo + min(jt, cur.n_tiles - 1)) * kBc;
     const int rows = min(kBc, n_keys - key0);
     const unsigned long long gsrc = uniform_addr(vh + (long long)key0 * G::kRowBytes);
     const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
@@ -1111,6 +1167,25 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     __builtin_amdgcn_s_waitcnt(0xC07F);
   };
 
+  // ---- the next item, prefetched during the current item's last P V
+  // product: its K tiles 0 and 1 into K ring slots 0 and 1, its Q rows into
+  // qf.
+  bool pref = false;
+  int nxt = -1;
+  Item nx = cur;
+  auto prefetch = [&]() __attribute__((always_inline)) {
+    if (pref) {
+      const char* const kbase = (const char*)(k + (long long)(nx.bh / group) * N * D);
+#pragma unroll
+      for (int kk = 0; kk < kCopyK; ++kk)
+        if (wave + kk * kW4 < G::kInstK) {
+          copy_k_of(kbase, nx.j_lo, nx.n_tiles, 0, 0, kk);
+          copy_k_of(kbase, nx.j_lo, nx.n_tiles, 1, 1, kk);
+        }
+      load_q((long long)nx.bh * N * D, nx.t * kBr4 + 32 * wave);
+    }
+  };
+
   // ---- LDS operand addresses: a per-lane base register plus an immediate
   // (ring slots are compile-time constants in the unrolled tile loop)
   const int k_lane = (int)lds_offset_of(lds_k) + l32 * G::kStrideK + 16 * half;
@@ -1122,10 +1197,6 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     v_lane[db] = (int)lds_offset_of(lds_v) + v_row * G::kStrideV + v_col + 64 * (db ^ G::vswz(v_row));
 
   f32x16 oacc[G::kDBlocks];
-#pragma unroll
-  for (int db = 0; db < G::kDBlocks; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   f32x16 sA[2], sB[2];      // score tiles S_j (being turned into P) and S_{j+1} (being computed)
   u32x4 pk[2][2];           // P as bf16 pairs (P_j, produced by tile j's stream)
   float m = 0.f, mc = 0.f;  // reference max of the row (raw score units) and m*c
@@ -1139,15 +1210,17 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // One key tile's stream.  HAS_PV: O^T += V_{j-1}^T P_{j-1}^T;  HAS_S:
   // snext = K_{j+1} Q^T;  SOFT: P_j = exp2(S_j*c - m*c) from scur into pk,
   // with the row sums of the fp32 and of the bf16-rounded P;  copy_kv: bit 0
-  // K_{j+2}, bit 1 V_j.  The sched_barrier after every MFMA and the empty asm
-  // statements that use each softmax step's results keep the interleave the
-  // source order states (the compiler would otherwise gather the VALU work).
+  // K_{j+2}, bit 1 V_j, bit 2 the next item's prefetch (at the first MFMA).
+  // The sched_barrier after every MFMA and the empty asm statements that use
+  // each softmax step's results keep the interleave the source order states
+  // (the compiler would otherwise gather the VALU work).
   auto stream = [&](int j, auto slot, f32x16 (&scur)[2], f32x16 (&snext)[2],
                     auto has_pv, auto has_s, auto soft, auto copy_kv, float& tsum, float& tbsum) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;  // j % 2
     constexpr bool HAS_PV = decltype(has_pv)::value, HAS_S = decltype(has_s)::value;
     constexpr bool SOFT = decltype(soft)::value;
     constexpr bool COPY_K = decltype(copy_kv)::value & 1, COPY_V = (decltype(copy_kv)::value & 2) != 0;
+    constexpr bool PREF = (decltype(copy_kv)::value & 4) != 0;
     constexpr int kNT = (HAS_PV ? kNP : 0) + (HAS_S ? kNS : 0);
     constexpr int kKOff = ((SL + 1) % kRing2) * G::kTileK;  // K_{j+1}
     constexpr int kVOff = ((SL + 1) % kRing2) * G::kTileV;  // V_{j-1}
@@ -1236,6 +1309,9 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
             if constexpr (COPY_V) copy_v(j, SL, cc - kMainK);
           }
         }
+      if constexpr (PREF) {
+        if (n == 0) prefetch();
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (SOFT && kNT == 0) {
@@ -1252,15 +1328,15 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // whole (window / causal edges, the ragged end of the sequence).  Element i
   // of block kb holds key 64*ja + 32*kb + 8*(i/4) + 4*half + (i%4).
   auto mask_tile = [&](int j, f32x16 (&sc)[2]) __attribute__((always_inline)) {
-    const int ja = j_lo + j;
-    if (ja < jf_lo || ja >= jf_hi) {
+    const int ja = cur.j_lo + j;
+    if (ja < cur.jf_lo || ja >= cur.jf_hi) {
       const int key0 = ja * kBc;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          sc[kb][i] = (key >= key_lo) & (key <= key_hi) ? sc[kb][i] : -INFINITY;
+          sc[kb][i] = ((key >= key_lo) & (key <= key_hi)) ? sc[kb][i] : -INFINITY;
         }
     }
   };
@@ -1318,6 +1394,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   using C0 = std::integral_constant<int, 0>;   // no copies
   using CV = std::integral_constant<int, 2>;   // V copies only
   using CKV = std::integral_constant<int, 3>;  // K and V copies
+  using CP = std::integral_constant<int, 4>;   // the next item's prefetch
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   // all of this wavefront's copy instructions of K tile jt
@@ -1326,16 +1403,6 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     for (int kk = 0; kk < kCopyK; ++kk)
       if (wave + kk * kW4 < G::kInstK) copy_k(jt, slot, kk);
   };
-  // ---- prologue: K_0 and K_1 in LDS, S_0 computed
-  copy_k_all(0, 0);
-  copy_k_all(1, 1);
-  wait_vmem(0);
-  __syncthreads();
-  {
-    float d0, d1;
-    stream(-1, S1{}, sB, sA, F_{}, T_{}, F_{}, C0{}, d0, d1);  // "tile -1": S_0 (slot 0) into sA
-  }
-  __syncthreads();  // B_0: nobody reads K_0 any more
 
   // Key tile j (ring slot SL = j % 2; S_j in sA for even j, sB for odd).
   auto tile = [&](int j, auto slot, auto has_pv, auto has_s, auto cp) __attribute__((always_inline)) {
@@ -1353,46 +1420,142 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     wait_vmem(0);
     __syncthreads();  // B_{j+1}
   };
-  // Tiles past tile 0 go in pairs (ring slots 1, 0); a lone last tile
-  // computes no S and copies no K.  (When the last tile ends a pair it
-  // computes an unused S and its K copy fetches the last tile again.)
-  tile(0, S0{}, F_{}, T_{}, CKV{});
-  int j = 1;
-  for (; j + 1 < n_tiles; j += 2) {
-    tile(j, S1{}, T_{}, T_{}, CKV{});
-    tile(j + 1, S0{}, T_{}, T_{}, CKV{});
-  }
-  if (j < n_tiles) tile(j, S1{}, T_{}, F_{}, CV{});
-  // the last O += V P: P_{n-1} with V_{n-1} (a stream "at tile n")
-  {
-    float d0, d1;
-    if (n_tiles & 1) stream(n_tiles, S1{}, sA, sB, T_{}, F_{}, F_{}, C0{}, d0, d1);
-    else stream(n_tiles, S0{}, sA, sB, T_{}, F_{}, F_{}, C0{}, d0, d1);
-  }
-  wait_vmem(0);
 
-  // ---- finalise: one division per row (by the sum of the rounded P the
-  // products used), then O and LSE = ln2 * (m*c + log2 l)
-  const float lt = sum_halves(l);
-  const float ltb = sum_halves(lb);
-  if (qrow >= N) return;
-  const float inv = ltb > 0.f ? 1.0f / ltb : 0.f;
-  const long long orow = head + (long long)qrow * D;
+  // Stores of one item: exactly kStores vector-memory instructions per
+  // wavefront (rows past N are dropped by the buffer range, not by a
+  // branch), so that the next item can wait for its prefetch alone.
+  constexpr int kStores = (kRows * D * (OUT_BF16 ? 2 : 4)) / 1024 + 1;  // 1 KiB of O per instruction, then LSE
+  bool prefetched = false;
+  for (int r = 0;; ++r) {
+    enter();
 #pragma unroll
-  for (int db = 0; db < G::kDBlocks; ++db)
+    for (int db = 0; db < G::kDBlocks; ++db)
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int dcol = 32 * db + 8 * a4 + 4 * half;
-      const float x0 = oacc[db][4 * a4 + 0] * inv, x1 = oacc[db][4 * a4 + 1] * inv;
-      const float x2 = oacc[db][4 * a4 + 2] * inv, x3 = oacc[db][4 * a4 + 3] * inv;
-      if (OUT_BF16) {
-        bf16x4 y = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
-        *(u32x2*)((__bf16*)o + orow + dcol) = __builtin_bit_cast(u32x2, y);
-      } else {
-        *(float4*)((float*)o + orow + dcol) = make_float4(x0, x1, x2, x3);
+      for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+    m = 0.f;
+    mc = 0.f;
+    m_set = false;
+    l = 0.f;
+    lb = 0.f;
+    // ---- prologue: K_0 and K_1 in LDS, S_0 computed
+    if (!prefetched) {
+      load_q(head, qw);
+      copy_k_all(0, 0);
+      copy_k_all(1, 1);
+      wait_vmem(0);
+    } else {
+      wait_vmem_n<kStores>();  // the prefetch, not the previous item's stores
+    }
+    __syncthreads();
+    {
+      float d0, d1;
+      stream(-1, S1{}, sB, sA, F_{}, T_{}, F_{}, C0{}, d0, d1);  // "tile -1": S_0 (slot 0) into sA
+    }
+    __syncthreads();  // B_0: nobody reads K_0 any more
+
+    if (PERSIST) {
+      nxt = item_of(r + 1);
+      pref = nxt >= 0;
+      if (nxt >= 0) nx = geom(nxt);
+    }
+    // Tiles past tile 0 go in pairs (ring slots 1, 0); a lone last tile
+    // computes no S and copies no K.  (When the last tile ends a pair it
+    // computes an unused S and its K copy fetches the last tile again.)
+    tile(0, S0{}, F_{}, T_{}, CKV{});
+    int j = 1;
+    for (; j + 1 < cur.n_tiles; j += 2) {
+      tile(j, S1{}, T_{}, T_{}, CKV{});
+      tile(j + 1, S0{}, T_{}, T_{}, CKV{});
+    }
+    if (j < cur.n_tiles) tile(j, S1{}, T_{}, F_{}, CV{});
+    // the last O += V P: P_{n-1} with V_{n-1} (a stream "at tile n")
+    {
+      float d0, d1;
+      using CF = std::conditional_t<PERSIST, CP, C0>;
+      if (cur.n_tiles & 1) stream(cur.n_tiles, S1{}, sA, sB, T_{}, F_{}, F_{}, CF{}, d0, d1);
+      else stream(cur.n_tiles, S0{}, sA, sB, T_{}, F_{}, F_{}, CF{}, d0, d1);
+    }
+
+    // ---- finalise: one division per row (by the sum of the rounded P the
+    // products used), then O and LSE = ln2 * (m*c + log2 l)
+    const float lt = sum_halves(l);
+    const float ltb = sum_halves(lb);
+    const float inv = ltb > 0.f ? 1.0f / ltb : 0.f;
+    const int rows = max(0, min(kRows, N - qw));
+    constexpr int kEsz = OUT_BF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc((const char*)o + (head + (long long)min(qw, N) * D) * kEsz, rows * D * kEsz);
+    // O goes out through LDS: the accumulator layout gives a lane 16-byte
+    // pieces of one row, so a direct store instruction would write 32-byte
+    // pieces of 32 rows; staged, each store instruction writes whole rows.
+    // The stage is this wave's quarter of the V ring (free once every wave is
+    // past its last P V product: the barrier below); rows of kStageCols
+    // columns, their 16-byte units XOR-permuted by the row so that the
+    // column-wise writes of the 32 rows spread over the banks.
+    constexpr int kStageBytes = kRing2 * G::kTileV / kW4;          // per wave
+    constexpr int kStageCols = kStageBytes / (kRows * kEsz);        // columns per pass
+    constexpr int kPasses = D / kStageCols;
+    constexpr int kUnits = kStageCols * kEsz / 16;                  // 16-byte units per staged row
+    constexpr int kRowsPerRead = 64 / kUnits;                       // rows per 64-lane read
+    static_assert(kStageCols % 32 == 0 && D % kStageCols == 0 && kUnits <= 64 && 64 % kUnits == 0, "stage shape");
+    char* const stage = lds_v + wave * kStageBytes;
+    __syncthreads();  // every wave's last P V product has read the V ring
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+#pragma unroll
+      for (int dbl = 0; dbl < kStageCols / 32; ++dbl) {
+        const int db = ps * (kStageCols / 32) + dbl;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int col = 32 * dbl + 8 * a4 + 4 * half;  // first of this lane's 4 columns within the pass
+          const int unit = (col * kEsz / 16) ^ (l32 % kUnits);
+          char* const dst = stage + l32 * (kStageCols * kEsz) + unit * 16 + (col * kEsz) % 16;
+          const float x0 = oacc[db][4 * a4 + 0] * inv, x1 = oacc[db][4 * a4 + 1] * inv;
+          const float x2 = oacc[db][4 * a4 + 2] * inv, x3 = oacc[db][4 * a4 + 3] * inv;
+          if (OUT_BF16) {
+            const bf16x4 y = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+            *(__attribute__((address_space(3))) u32x2*)(size_t)lds_offset_of(dst) = __builtin_bit_cast(u32x2, y);
+          } else {
+            const u32x4 y = {__float_as_uint(x0), __float_as_uint(x1), __float_as_uint(x2), __float_as_uint(x3)};
+            *(__attribute__((address_space(3))) u32x4*)(size_t)lds_offset_of(dst) = y;
+          }
+        }
+      }
+#pragma unroll
+      for (int rd = 0; rd < kRows / kRowsPerRead; ++rd) {
+        const int row = rd * kRowsPerRead + lane / kUnits, unit = lane % kUnits;
+        const u32x4 y = *(const __attribute__((address_space(3))) u32x4*)(size_t)lds_offset_of(
+            stage + row * (kStageCols * kEsz) + (unit ^ (row % kUnits)) * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(y, ro, row * (D * kEsz) + ps * (kStageCols * kEsz) + unit * 16, 0, 0);
       }
     }
-  if (half == 0) lse[(long long)bh * N + qrow] = (m * c + log2f(lt)) * 0.69314718055994531f;
+    // both halves of a row hold the same LSE; both store it
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (long long)cur.bh * N + min(qw, N), rows * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m * c + log2f(lt)) * 0.69314718055994531f), rl, l32 * 4,
+                                          0, 0);
+    if (!PERSIST || nxt < 0) break;
+    prefetched = pref;
+    cur = nx;
+  }
+}
+
+// Compute units of the current device (looked up once per device).
+hipError_t compute_units(int* units) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> by_device[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int n = by_device[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n <= 0) return hipErrorInvalidValue;
+    by_device[dev].store(n, std::memory_order_relaxed);
+  }
+  *units = n;
+  return hipSuccess;
 }
 
 template <int D, bool MASKED, bool OUT_BF16, bool SPARSE, bool PAGED = false, bool FP8 = false>
@@ -1408,11 +1571,16 @@ hipError_t launch_t(const FwdArgs& a) {
     if (a.items == nullptr) {
       // plain, causal and sliding-window forward: the 128-row kernel
       const int T4 = (a.N + kBr4 - 1) / kBr4;
-      const long long grid4 = (long long)T4 * a.B * a.H;
-      if (grid4 > 0x7fffffffLL) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((fwd_kernel<D, MASKED, OUT_BF16>), dim3((unsigned)grid4), dim3(kThreads4), 0, a.stream,
-                         (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, a.B * a.H, a.N, T4, c,
-                         a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr);
+      const long long items = (long long)T4 * a.B * a.H;
+      if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+      int units = 0;
+      const hipError_t eu = compute_units(&units);
+      if (eu != hipSuccess) return eu;
+      const FwdSchedule sc = fwd_schedule(items, units, MASKED && a.wl < 0, D);
+      auto kern = sc.sched == 0 ? fwd_kernel<D, MASKED, OUT_BF16, false> : fwd_kernel<D, MASKED, OUT_BF16, true>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)sc.workgroups), dim3(kThreads4), 0, a.stream, (const __bf16*)a.q,
+                         (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, a.B * a.H, a.N, T4, c, a.poison ? 1 : 0,
+                         a.H / a.Hkv, a.wl, a.wr, (int)items, sc.sched);
       return hipGetLastError();
     }
   }

@@ -83,6 +83,32 @@ constexpr int kBf16BlockCols = 64;
 // paged and FP8 modes.)
 constexpr int kFwdWaves = 4;
 constexpr int kFwdBlockRows = kFwdWaves * 32;  // 128
+
+// How that kernel's items ((query tile, batch*head) pairs) go to workgroups,
+// two of which fit a compute unit.  sched 0: one item per workgroup (the
+// hardware hands out items as units free up); 1: equal items in rounds,
+// workgroup g taking g, g + G, ... (G a multiple of 8, so that a workgroup
+// keeps to one XCD's items) when there are more than the units hold at
+// once (used at d = 64, where it measured faster; at d = 128 the loop
+// over items costs the kernel registers it does not have to spare); 2:
+// items of growing length (a causal mask or a window open to the left),
+// more than one per unit but at most two: G = ceil(items / 2) workgroups
+// each take the i-th heaviest and the i-th lightest item.
+struct FwdSchedule {
+  long long workgroups;
+  int sched;
+};
+inline FwdSchedule fwd_schedule(long long items, int units, bool uneven, int d) {
+  const long long slots = 2LL * units;
+  if (!uneven && d == 64 && items > slots) {
+    const long long rounds = (items + slots - 1) / slots;
+    long long groups = (items + rounds - 1) / rounds;
+    groups = (groups + 7) / 8 * 8;
+    return {groups, 1};
+  }
+  if (uneven && items > units && items <= slots) return {(items + 1) / 2, 2};
+  return {items, 0};
+}
 constexpr int kF32Waves = 4;
 constexpr int kF32BlockRows = kF32Waves * 32;    // 128
 constexpr int kF32BlockCols = 32;

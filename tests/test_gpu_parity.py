@@ -150,6 +150,78 @@ def test_workload_full_size(name, seed):
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
 
 
+# --- the kernel's item schedules ----------------------------------------------
+# fa2_fwd hands (query tile, batch*head) items of 128 rows to workgroups in
+# one of three ways, picked from the item count and the device's compute
+# units (256 on an MI355X, two workgroups each): one item per workgroup;
+# equal items in rounds (d = 64, more than 512 items; the next item's first
+# K tiles and Q rows are loaded while the current one finishes); causal
+# items paired heaviest with lightest (257 to 512 items).  These shapes put
+# each way through every element (ragged rounds, ragged tails, head counts
+# that are and are not multiples of 8, grouped heads, bf16 O).
+
+def _units():
+    return torch.cuda.get_device_properties(DEV).multi_processor_count
+
+
+SCHED_EQUAL = [
+    # B, H, N: d = 64, unmasked, items = B*H*ceil(N/128) > 2 * units
+    (4, 37, 1000),   # 1,184 items: three rounds, the last one short; B*H not a multiple of 8
+    (8, 16, 600),    # 640 items, B*H a multiple of 8 (XCD-major order)
+    (3, 50, 513),    # 750 items, one row past a tile edge
+]
+
+
+@pytest.mark.parametrize("o_bf16", [False, True])
+@pytest.mark.parametrize("B,H,N", SCHED_EQUAL, ids=[f"{b}x{h}x{n}" for b, h, n in SCHED_EQUAL])
+def test_schedule_equal_items_in_rounds(B, H, N, o_bf16):
+    items = B * H * -(-N // 128)
+    print(f"[case] rounds of equal items {B}x{H}x{N}x64: {items} items on {_units()} units, "
+          f"o {'bf16' if o_bf16 else 'fp32'}", flush=True)
+    q, k, v = _inputs(B, H, N, 64, "bf16", seed=B * H + N)
+    o, lse = _run(q, k, v, False, 0.125, torch.bfloat16 if o_bf16 else torch.float32)
+    eo, el = ref.attention_ref(_np64(q), _np64(k), _np64(v), 0.125, False)
+    _check(o, lse, eo, el, "bf16", f"rounds {B}x{H}x{N}", o_bf16=o_bf16)
+
+
+SCHED_PAIRS = [
+    # B, H, H_kv, N, d, window: causal-like items, units < items <= 2 * units
+    (2, 3, 3, 6000, 64, (-1, 0)),     # 282 items
+    (1, 6, 2, 5000, 64, (-1, 0)),     # 240 items: one per workgroup (fewer than the units)
+    (1, 6, 2, 6100, 64, (-1, 0)),     # 288 items, grouped heads
+    (1, 5, 5, 7000, 64, (-1, 37)),    # window open to the left: 275 items
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,window", SCHED_PAIRS,
+                         ids=[f"{b}x{h}/{hk}x{n}x{d}-w{w[0]}_{w[1]}" for b, h, hk, n, d, w in SCHED_PAIRS])
+def test_schedule_paired_causal_items(B, H, H_kv, N, d, window):
+    items = B * H * -(-N // 128)
+    print(f"[case] paired items {B}x{H}/{H_kv}x{N}x{d} window {window}: {items} items on {_units()} units",
+          flush=True)
+    q, k, v = _inputs(B, H, N, d, "bf16", seed=N + H, outliers=0.001)
+    k, v = k[:, :H_kv].contiguous(), v[:, :H_kv].contiguous()
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa2.forward(q, k, v, scale=scale, window=window)
+    torch.cuda.synchronize()
+    eo, el = ref.attention_ref_window(_np64(q), _np64(k), _np64(v), scale, *window)
+    _check(o, lse, eo, el, "bf16", f"pairs {B}x{H}/{H_kv}x{N}x{d} window {window}")
+
+
+def test_schedule_paired_causal_items_d128_sampled():
+    """d = 128, 282 causal items (paired): sampled rows of every head."""
+    B, H, N = 1, 3, 12000
+    print(f"[case] paired items {B}x{H}x{N}x128 causal, sampled rows", flush=True)
+    q, k, v = _inputs(B, H, N, 128, "bf16", seed=77, outliers=0.001)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _run(q, k, v, True, scale)
+    rng = np.random.default_rng(5)
+    for h in range(H):
+        rows = _sample_rows(N, rng)
+        eo, el = ref.attention_rows(_np64(q[0, h]), _np64(k[0, h]), _np64(v[0, h]), scale, True, rows)
+        _check(o[0, h][rows], lse[0, h][rows], eo, el, "bf16", f"pairs d128 head {h} {len(rows)} rows")
+
+
 # --- closed forms and invariants on the GPU -----------------------------------
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
