@@ -94,17 +94,61 @@ PEAK_F32_TFLOPS = 157.3
 # Dense FP8 matrix-core peak (E4M3 x E4M3, fp32 accumulation): twice bf16.
 PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 PEAK_HBM_GBS = 8000.0
-BWD_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_bwd_bf16.hip",
-               "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
-               "exact_tiled_attention_33_amd/csrc/fa2_launch.h"]
-KERNEL_SOURCES = ["exact_tiled_attention_33_amd/csrc/fa2_fwd_bf16.hip",
-                  "exact_tiled_attention_33_amd/csrc/fa2_fwd_f32.hip",
-                  "exact_tiled_attention_33_amd/csrc/fa2_api.cpp",
-                  "exact_tiled_attention_33_amd/csrc/fa2_launch.h"]
+# Sources (and the build script with its compile flags) behind each measured
+# kernel: a profile summary stamped with the hash of its list is current only
+# while none of them changes.
+_CSRC = "exact_tiled_attention_33_amd/csrc/"
+_COMMON = [_CSRC + "fa2_api.cpp", _CSRC + "fa2_launch.h", "exact_tiled_attention_33_amd/build_lib.py"]
+KERNEL_SOURCES = [_CSRC + "fa2_fwd_bf16.hip", _CSRC + "fa2_fwd_f32.hip"] + _COMMON
+BWD_SOURCES = [_CSRC + "fa2_bwd_bf16.hip"] + _COMMON
+DECODE_SOURCES = [_CSRC + "fa2_decode.hip", _CSRC + "fa2_fwd_bf16.hip"] + _COMMON  # merge kernel in the latter
+FP8_SOURCES = [_CSRC + "fa2_fp8.hip", _CSRC + "fa2_fwd_bf16.hip"] + _COMMON
 CALIB_BYTES = 1 << 30
 ROTATE_BYTES = 512 * 10**6  # rotated input/output sets span at least this (twice the 256 MB MALL)
 METRIC_DECODE = "paged-KV decode, GB/s of key/value traffic vs MI355X HBM peak"
 DECODE_CONFIG = {"B": 64, "H": 32, "H_kv": 8, "d": 128, "n_q": 1, "page_size": 64, "L_min": 1024, "L_max": 8192}
+
+
+def idle_clock(fa2):
+    """Shader clock (GHz) of 256 probe workgroups on an otherwise idle GPU."""
+    try:
+        return round(fa2.shader_clock_ghz(), 3)
+    except Exception:  # pragma: no cover - diagnostic only
+        return None
+
+
+def warm_step_ms(events):
+    """Median GPU time of one warm-up step (events recorded between steps),
+    or 0.1 ms without warm-up steps."""
+    if len(events) < 2:
+        return 0.1
+    return statistics.median(a.elapsed_time(b) for a, b in zip(events[:-1], events[1:]))
+
+
+def start_probe(fa2, seconds):
+    """One probe workgroup on a stream of its own, started just ahead of the
+    timed launches, for 80% of the timed region's expected length `seconds`
+    (so that it ends inside the region and the synchronisation that closes
+    the region never waits for it); None if it cannot start."""
+    try:
+        p = fa2.ClockProbe(1)
+        p.start(0.8 * seconds)
+        return p
+    except Exception:  # pragma: no cover - diagnostic only
+        return None
+
+
+def clock_report(idle_before, probe, idle_after):
+    during = None
+    if probe is not None:
+        try:
+            during = round(probe.ghz(), 3)
+        except Exception:  # pragma: no cover
+            during = None
+    return {"during_timed_ghz": during, "idle_before_ghz": idle_before, "idle_after_ghz": idle_after,
+            "probe": "fa2_clock_probe: shader cycles (s_memtime) against the 100 MHz reference (s_memrealtime); "
+                     "during = one single-wave workgroup on its own stream over the first 80% of the timed region "
+                     "(it takes one wave slot of the chip); idle = 256 workgroups for 50 us before and after it"}
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -287,13 +331,19 @@ def run_bench(args) -> dict:
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st)
 
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
+    wev[0].record(stream)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
+            wev[i + 1].record(stream)
     torch.cuda.synchronize()
+    warm_ms = warm_step_ms(wev)
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    clk_before = idle_clock(fa2)
+    probe = start_probe(fa2, args.steps * warm_ms * 1e-3)
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -301,6 +351,7 @@ def run_bench(args) -> dict:
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = clock_report(clk_before, probe, idle_clock(fa2))
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     span_ms = starts[0].elapsed_time(ends[-1])
@@ -400,7 +451,8 @@ def run_bench(args) -> dict:
                    "input_sets": n_sets, "input_set_bytes": set_bytes},
         "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count},
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "shader_clock": clock,
+        "kernel_source_sha256_16": kernel_source_hash(FP8_SOURCES if fp8_kernel is not None else None),
         "context_not_target": "pages (A100): FA1 25-40% of peak, FA2 50-73% of peak, up to 230 TFLOP/s",
     }
     if not args.no_cpu_baseline and args.window is None and sparse_pairs is None and fp8_kernel is None:
@@ -479,11 +531,17 @@ def run_bench_bwd(args) -> dict:
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st, "fa2_bwd")
 
-    for _ in range(args.warmup):
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
+    wev[0].record(stream)
+    for i in range(args.warmup):
         step()
+        wev[i + 1].record(stream)
     torch.cuda.synchronize()
+    warm_ms = warm_step_ms(wev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    clk_before = idle_clock(fa2)
+    probe = start_probe(fa2, args.steps * warm_ms * 1e-3)
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -491,6 +549,7 @@ def run_bench_bwd(args) -> dict:
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = clock_report(clk_before, probe, idle_clock(fa2))
     per_call_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_ms = sum(per_call_ms) / len(per_call_ms)
     pairs = workloads.credited_pairs(w.N, wl, wr)
@@ -536,6 +595,7 @@ def run_bench_bwd(args) -> dict:
                    "per_call_ms_max": round(max(per_call_ms), 4)},
         "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count},
+        "shader_clock": clock,
         "kernel_source_sha256_16": kernel_source_hash(BWD_SOURCES),
     }
     if not args.no_cpu_baseline and args.window is None:
@@ -578,11 +638,17 @@ def run_bench_decode(args) -> dict:
         if st != fa2.FA2_OK:
             raise fa2.Fa2Error(st, "fa2_decode_paged")
 
-    for _ in range(args.warmup):
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
+    wev[0].record(stream)
+    for i in range(args.warmup):
         step()
+        wev[i + 1].record(stream)
     torch.cuda.synchronize()
+    warm_ms = warm_step_ms(wev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    clk_before = idle_clock(fa2)
+    probe = start_probe(fa2, args.steps * warm_ms * 1e-3)
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -590,6 +656,7 @@ def run_bench_decode(args) -> dict:
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = clock_report(clk_before, probe, idle_clock(fa2))
     per_launch_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     avg_ms = sum(per_launch_ms) / len(per_launch_ms)
     kv_bytes = 2 * sum(lens) * cfg["H_kv"] * cfg["d"] * 2
@@ -613,7 +680,8 @@ def run_bench_decode(args) -> dict:
         "timing": {"per_launch_ms_min": round(min(per_launch_ms), 4),
                    "per_launch_ms_max": round(max(per_launch_ms), 4)},
         "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "shader_clock": clock,
+        "kernel_source_sha256_16": kernel_source_hash(DECODE_SOURCES),
     }
 
 

@@ -58,7 +58,7 @@ __all__ = [
     "fa2_split_plan", "fa2_fwd_split", "SplitPlan", "split_plan", "forward_split",
     "fa2_sparse_plan", "fa2_fwd_sparse", "SparsePlan", "forward_sparse",
     "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_decode_paged_noalloc", "decode_paged",
-    "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fp8_pack", "forward_fp8",
+    "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fp8_pack", "forward_fp8", "fa2_clock_probe", "ClockProbe", "shader_clock_ghz",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -77,7 +77,7 @@ FA2_DECODE_SCRATCH_BYTES = 16 << 20
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_gqa", "fa2_fwd_window", "fa2_bwd", "fa2_bwd_gqa",
                     "fa2_bwd_window", "fa2_plan", "fa2_split_plan", "fa2_fwd_split", "fa2_sparse_plan",
                     "fa2_fwd_sparse", "fa2_decode_paged_workspace", "fa2_decode_paged", "fa2_decode_paged_noalloc",
-                    "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fa2_strerror", "fa2_version")
+                    "fa2_fp8_pack_workspace", "fa2_fp8_pack", "fa2_fwd_fp8", "fa2_clock_probe", "fa2_strerror", "fa2_version")
 
 _LIB_PATH = Path(__file__).resolve().parent / "libfa2.so"
 _lib = None
@@ -292,6 +292,8 @@ def load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
     ]
+    lib.fa2_clock_probe.restype = ctypes.c_int
+    lib.fa2_clock_probe.argtypes = [ctypes.c_int, ctypes.c_ulonglong, ctypes.c_void_p, ctypes.c_void_p]
     lib.fa2_strerror.restype = ctypes.c_char_p
     lib.fa2_strerror.argtypes = [ctypes.c_int]
     lib.fa2_version.restype = ctypes.c_int
@@ -463,6 +465,44 @@ def fa2_fwd_fp8(q8, q_scale, k8, k_scale, v, o, lse, B, H, H_kv, N, d, causal, s
     """Raw C call: pointers and sizes as Python ints; returns the status code."""
     return int(load().fa2_fwd_fp8(q8, q_scale, k8, k_scale, v, o, lse, B, H, H_kv, N, d, int(causal),
                                   float(scale), stream, o_dtype))
+
+
+def fa2_clock_probe(workgroups, ticks, out, stream) -> int:
+    """Raw C call: out is a device pointer (int) to 3 * workgroups uint64."""
+    return int(load().fa2_clock_probe(int(workgroups), int(ticks), out, stream))
+
+
+class ClockProbe:
+    """fa2_clock_probe on a stream of its own: ``start(seconds)`` enqueues one
+    workgroup that runs for that long beside whatever else runs, ``ghz()``
+    waits for it and returns the mean shader clock over its span."""
+
+    def __init__(self, workgroups: int = 1, device=None):
+        import torch
+
+        self.dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.workgroups = workgroups
+        self.out = torch.zeros(3 * workgroups, dtype=torch.int64, device=self.dev)
+        self.stream = torch.cuda.Stream(device=self.dev)
+
+    def start(self, seconds: float) -> None:
+        ticks = max(1, min(10**9, int(seconds * 1e8)))
+        st = fa2_clock_probe(self.workgroups, ticks, self.out.data_ptr(), self.stream.cuda_stream)
+        if st != FA2_OK:
+            raise Fa2Error(st, "fa2_clock_probe")
+
+    def ghz(self) -> float:
+        self.stream.synchronize()
+        t = self.out.view(-1, 3).cpu()
+        return 0.1 * float(t[:, 0].sum()) / float(t[:, 1].sum())
+
+
+def shader_clock_ghz(workgroups: int = 256, seconds: float = 50e-6) -> float:
+    """Mean shader clock (GHz) of `workgroups` probe workgroups that each run
+    for `seconds` on an otherwise idle stream."""
+    p = ClockProbe(workgroups)
+    p.start(seconds)
+    return p.ghz()
 
 
 def fa2_strerror(status: int) -> str:

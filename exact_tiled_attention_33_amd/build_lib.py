@@ -20,7 +20,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libfa2.so"
-SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_f32.hip", "fa2_bwd_bf16.hip", "fa2_fp8.hip", "fa2_decode.hip"]
+SOURCES = ["fa2_api.cpp", "fa2_fwd_bf16.hip", "fa2_fwd_f32.hip", "fa2_bwd_bf16.hip", "fa2_fp8.hip", "fa2_decode.hip", "fa2_probe.hip"]
 
 ARCH = "gfx950"
 COMMON = [

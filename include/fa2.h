@@ -595,6 +595,26 @@ typedef struct fa2_plan_t {
 int fa2_plan(int B, int H, int N, int d, int causal, int in_dtype,
              int block_rows, int block_cols, int num_units, fa2_plan_t* out);
 
+/*
+ * fa2_clock_probe -- measure the shader clock on the device (a diagnostic
+ * for benchmarks, not part of the attention path).
+ *
+ * Enqueues `workgroups` one-wavefront workgroups on `stream`; each runs a
+ * dependent chain of VALU work until the 100 MHz reference counter has
+ * advanced by `ticks` (10 ns each), then workgroup g writes to
+ * out[3g .. 3g+2] how far the shader cycle counter and the reference
+ * counter advanced, and a value that keeps the chain from being optimised
+ * away.  The mean clock is 100 MHz * sum(out[3g]) / sum(out[3g+1]).  On a
+ * stream of its own, beside other work, a single workgroup measures the
+ * clock under that work.
+ *
+ *   workgroups  1 .. 65536;  ticks  1 .. 10^9 (10 s).
+ *   out         device, 8-byte aligned, 3 * workgroups uint64, overwritten.
+ * Returns FA2_OK after enqueueing, FA2_ERR_INVALID_ARG, FA2_ERR_NO_DEVICE
+ * or FA2_ERR_LAUNCH.
+ */
+int fa2_clock_probe(int workgroups, unsigned long long ticks, unsigned long long* out, void* stream);
+
 /* fa2_strerror -- static, NUL-terminated description of a status code. */
 const char* fa2_strerror(int status);
 

@@ -304,3 +304,16 @@ def test_bwd_window_validation():
     if not _gpu_present():
         assert _wbcall(5, 5) == fa2.FA2_ERR_NO_DEVICE
         assert _wbcall(-1, 0) == fa2.FA2_ERR_NO_DEVICE
+
+
+# --- the shader-clock probe (a benchmark diagnostic) -------------------------
+
+@pytest.mark.parametrize("groups, ticks, out", [(0, 10, 0x10000000), (65537, 10, 0x10000000), (4, 0, 0x10000000),
+                                                (4, 10**9 + 1, 0x10000000), (4, 10, 0), (4, 10, 0x10000004)])
+def test_clock_probe_rejects_before_any_hip_call(groups, ticks, out):
+    assert fa2.fa2_clock_probe(groups, ticks, out, 0) == fa2.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(_gpu_present(), reason="a valid fake pointer would launch on a real GPU")
+def test_clock_probe_no_device_status_on_cpu_only_host():
+    assert fa2.fa2_clock_probe(4, 10, 0x10000000, 0) == fa2.FA2_ERR_NO_DEVICE

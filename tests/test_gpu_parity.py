@@ -315,6 +315,14 @@ def test_error_status_on_gpu():
     assert e.value.status == fa2.FA2_ERR_UNSUPPORTED
 
 
+def test_shader_clock_probe_is_plausible():
+    """The benchmark's clock probe reads a clock between 0.3 and 3 GHz (the
+    MI355X's peak engine clock is 2.4 GHz)."""
+    ghz = fa2.shader_clock_ghz()
+    print(f"[probe] shader clock {ghz:.3f} GHz", flush=True)
+    assert 0.3 < ghz < 3.0
+
+
 def test_buffer_rejections_on_gpu():
     """A host or wrongly sized out/lse raises ValueError before any launch."""
     q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device=DEV)
