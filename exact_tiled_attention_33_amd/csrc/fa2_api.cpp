@@ -193,7 +193,7 @@ const char* fa2_strerror(int status) {
   switch (status) {
     case FA2_OK: return "success";
     case FA2_ERR_INVALID_ARG: return "invalid argument (null/misaligned/overlapping pointer, bad size, scale or dtype code)";
-    case FA2_ERR_UNSUPPORTED: return "unsupported configuration (forward: head dim 64 or 128; backward: bf16 inputs, head dim 128)";
+    case FA2_ERR_UNSUPPORTED: return "unsupported configuration (head dim 64 or 128; backward: bf16 inputs)";
     case FA2_ERR_NO_DEVICE: return "no HIP device available";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     case FA2_ERR_SCRATCH: return "the call needs more than the static scratch of a no-alloc entry point";
@@ -702,7 +702,7 @@ int fa2_bwd_window(const void* q, const void* k, const void* v, const void* o, c
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA2_ERR_INVALID_ARG;
   }
-  if (in_dtype != FA2_BF16 || d != 128) return FA2_ERR_UNSUPPORTED;
+  if (in_dtype != FA2_BF16 || (d != 64 && d != 128)) return FA2_ERR_UNSUPPORTED;
 
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA2_ERR_NO_DEVICE;

@@ -30,14 +30,14 @@
 //    dQ^T += K^T dS^T consumes dS^T in the same relabelled layout.
 // No atomics: every output element is written by exactly one wavefront.
 //
-// LDS tiles hold rows of 256 bytes (d = 128) with no padding.  A tile is
-// read both along rows (16-byte operand reads: 16 lanes, 16 rows, one
-// column) and across rows (ds_read_b64_tr_b16: 4 consecutive rows of a
+// LDS tiles hold rows of 2*d bytes (d = 64 or 128) with no padding.  A
+// tile is read both along rows (16-byte operand reads: 16 lanes, 16 rows,
+// one column) and across rows (ds_read_b64_tr_b16: 4 consecutive rows of a
 // 64-byte column block), so instead of padding, the 16-byte chunk c of row
-// r is stored at position c ^ swz(r) with swz(r) = 4*(r%4) + (r/4)%4: the
-// 16 rows of a row read land on 16 distinct chunk positions and the 4 rows
-// of a transposing read on 4 distinct 64-byte quarters of the 256-byte bank
-// line, so both are free of bank conflicts.  The permutation is applied on
+// r is stored at position c ^ swz(r) (BG below): the 16 rows of a row read
+// land on 16 distinct 16-byte slots and the 4 rows of a transposing read on
+// 4 distinct 64-byte quarters of the 256-byte bank line, so both are free
+// of bank conflicts.  The permutation is applied on
 // the global side of the global->LDS copies (each lane fetches the chunk
 // that belongs at its LDS slot).
 
@@ -60,13 +60,28 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int kD = 128;
-constexpr int kRowBytes = kD * 2;   // one LDS row (no padding)
-constexpr int kKSteps = kD / 16;    // k-steps of a d-contraction MFMA
-constexpr int kDBlocks = kD / 32;   // 32-row blocks of a d-sized accumulator
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Geometry of head dimension D (64 or 128): LDS rows of 2*D bytes (no
+// padding), the k-steps of a d-contraction MFMA and the 32-row blocks of a
+// d-sized accumulator.  The 16-byte chunk c of row r sits at position
+// c ^ swz(r).  D = 128 (16 chunks, one row per 256-byte bank line):
+// swz(r) = 4*(r%4) + (r/4)%4.  D = 64 (8 chunks, two rows per bank line):
+// swz(r) = (r/4)%4 + 4*((r/2)%2), which puts the 16 rows of a row-read
+// phase on the 16 distinct 16-byte slots of the bank line and the 4 rows of
+// a transposing read on its 4 distinct 64-byte quarters.
+template <int D>
+struct BG {
+  static_assert(D == 64 || D == 128, "head dimension 64 or 128");
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per row
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;  // rows per 64-lane x 16-byte copy
+  static constexpr int kKSteps = D / 16;
+  static constexpr int kDBlocks = D / 32;
+  static __device__ __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r >> 2) & 3) | (((r >> 1) & 1) << 2));
+  }
+};
 
 template <typename T>
 __device__ __forceinline__ T pin(T x) {
@@ -136,46 +151,54 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 //             multiples of 16 rows) in 64-byte column block db: lane i of
 //             each 16-lane group points at row i/4 of a 4-row slab and at
 //             columns 4*(i%4) .. +3 of a 16-column slab.
+template <int D>
 struct LdsOffsets {
-  int row[kKSteps];
-  int tr[kDBlocks][2];
+  int row[BG<D>::kKSteps];
+  int tr[BG<D>::kDBlocks][2];
 };
 
-__device__ __forceinline__ LdsOffsets lds_offsets(int lane) {
-  LdsOffsets o;
+template <int D>
+__device__ __forceinline__ LdsOffsets<D> lds_offsets(int lane) {
+  using Gm = BG<D>;
+  LdsOffsets<D> o;
   const int l32 = lane & 31, half = lane >> 5;
-  const int sw = swz(l32);
+  const int sw = Gm::swz(l32);
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s) o.row[s] = l32 * kRowBytes + 16 * ((2 * s + half) ^ sw);
+  for (int s = 0; s < Gm::kKSteps; ++s) o.row[s] = l32 * Gm::kRowBytes + 16 * ((2 * s + half) ^ sw);
   const int t4 = (lane & 15) >> 2;                          // row within the 4-row slab
   const int e = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // 16-byte chunk within the 64-byte block
+  // the slab's rows r = 4*half + t4 (+ 8u): their 64-byte block db sits at
+  // db ^ (bits 2-3 of swz(r)), the chunk within it at e ^ (bits 0-1)
+  const int bq = D == 128 ? t4 : (t4 >> 1);
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db)
+  for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      o.tr[db][u] = (4 * half + t4) * kRowBytes + 64 * (db ^ t4) + 16 * (e ^ (half + 2 * u)) + 8 * (lane & 1);
+      o.tr[db][u] = (4 * half + t4) * Gm::kRowBytes + 64 * (db ^ bq) + 16 * (e ^ (half + 2 * u)) + 8 * (lane & 1);
   return o;
 }
 
 // Source byte offset (relative to the tile's first row) of the chunk that a
 // lane of copy instruction i puts into LDS: instruction i fills rows
-// 4i .. 4i+3 (64 lanes x 16 bytes, in LDS order); swz of those rows depends
-// on the lane and on i % 4 only.
+// kRowsPerCopy*i .. +kRowsPerCopy-1 (64 lanes x 16 bytes, in LDS order).
+template <int D>
 __device__ __forceinline__ int copy_voff(int lane, int i) {
-  const int r = 4 * i + (lane >> 4);
-  return r * kRowBytes + 16 * ((lane & 15) ^ swz(r));
+  using Gm = BG<D>;
+  const int r = Gm::kRowsPerCopy * i + lane / Gm::kChunks;
+  return r * Gm::kRowBytes + 16 * ((lane % Gm::kChunks) ^ Gm::swz(r));
 }
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i: 16 lanes per row, 8 elements per lane.
-template <bool O_BF16>
+// D_i = dO_i . O_i: D/8 lanes per row, 8 elements per lane.
+template <int D, bool O_BF16>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__ o, const __bf16* __restrict__ dout,
                                                         float* __restrict__ delta, long long rows) {
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
+  constexpr int kLanes = D / 8;  // lanes per row
+  const long long row = (long long)blockIdx.x * (256 / kLanes) + (threadIdx.x / kLanes);
+  const int part = threadIdx.x % kLanes;
   float acc = 0.f;
   if (row < rows) {
-    const long long base = row * kD + part * 8;
+    const long long base = row * D + part * 8;
     const bf16x8 g = *(const bf16x8*)(dout + base);
     float ov[8];
     if (O_BF16) {
@@ -192,7 +215,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__
     for (int i = 0; i < 8; ++i) acc = fmaf((float)g[i], ov[i], acc);
   }
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  for (int m = kLanes / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kLanes);
   if (row < rows && part == 0) delta[row] = acc;
 }
 
@@ -202,19 +225,27 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void* __restrict__
 constexpr int kKVWaves = 8;
 constexpr int kKVKeys = kBwdKVKeys;                    // 128 = 4 waves x 32 keys
 constexpr int kQB = kBwdKVRows;                        // 32 queries per block
-constexpr int kKVTileBytes = kKVKeys * kRowBytes;      // 32 KiB (K or V)
-constexpr int kQBBytes = kQB * kRowBytes;              // 8 KiB (Q or dO block)
-constexpr int kSlotBytes = 2 * kQBBytes + 2 * 256;     // Q, dO, LSE row, D row
-constexpr int kKVLds = 2 * kKVTileBytes + 4 * kSlotBytes;  // 2 groups x 2 slots
-static_assert(kKVLds >= 4 * 128 * 64 * 4, "partial sums of one group must fit in LDS");
+template <int D>
+struct KVG {
+  static constexpr int kKVTileBytes = kKVKeys * BG<D>::kRowBytes;  // K or V tile: 32 KiB at d = 128
+  static constexpr int kQBBytes = kQB * BG<D>::kRowBytes;          // Q or dO block: 8 KiB at d = 128
+  static constexpr int kSlotBytes = 2 * kQBBytes + 2 * 256;        // Q, dO, LSE row, D row
+  static constexpr int kLds = 2 * kKVTileBytes + 4 * kSlotBytes;   // 2 groups x 2 slots
+  static constexpr int kAccVals = 2 * BG<D>::kDBlocks * 16;        // dV and dK values per lane
+  static_assert(kLds >= 4 * kAccVals * 64 * 4, "partial sums of one group must fit in LDS");
+};
 
-template <bool MASKED, bool GRAD_BF16>
+template <int D, bool MASKED, bool GRAD_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kKVWaves * 64, kKVWaves * 64), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                      const __bf16* __restrict__ dout, const float* __restrict__ lse,
                      const float* __restrict__ delta, void* __restrict__ dk, void* __restrict__ dv,
                      int BHkv, int N, float c, float scale, int group, int wl, int wr) {
-  __shared__ __attribute__((aligned(1024))) char smem[kKVLds];
+  using Gm = BG<D>;
+  constexpr int kD = D, kRowBytes = Gm::kRowBytes, kKSteps = Gm::kKSteps, kDBlocks = Gm::kDBlocks;
+  constexpr int kKVTileBytes = KVG<D>::kKVTileBytes, kQBBytes = KVG<D>::kQBBytes;
+  constexpr int kSlotBytes = KVG<D>::kSlotBytes, kAccVals = KVG<D>::kAccVals;
+  __shared__ __attribute__((aligned(1024))) char smem[KVG<D>::kLds];
   const char* const lds_k = smem;
   const char* const lds_v = smem + kKVTileBytes;
   char* const lds_ring = smem + 2 * kKVTileBytes;
@@ -241,17 +272,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int q_lo = (MASKED && wr >= 0) ? max(0, key - wr) : 0;
   const int q_hi = key >= N ? -1 : ((MASKED && wl >= 0) ? min(N - 1, key + wl) : N - 1);
 
-  // ---- K and V tiles (once): 32 copy instructions each, 4 per wave ----
+  // ---- K and V tiles (once): kKVKeys / kRowsPerCopy copy instructions each ----
   {
     const int rows = min(kKVKeys, N - k0);
     const i32x4 rk = raw_rsrc(k + head + (long long)k0 * kD, rows * kRowBytes);
     const i32x4 rv = raw_rsrc(v + head + (long long)k0 * kD, rows * kRowBytes);
     const unsigned base = __builtin_amdgcn_readfirstlane(lds_offset_of(smem));
 #pragma unroll
-    for (int m = 0; m < kKVKeys / 4 / kKVWaves; ++m) {
+    for (int m = 0; m < kKVKeys / Gm::kRowsPerCopy / kKVWaves; ++m) {
       const int i = wave + kKVWaves * m;
-      copy16_to_lds(rk, copy_voff(lane, i), base + 1024 * i);
-      copy16_to_lds(rv, copy_voff(lane, i), base + kKVTileBytes + 1024 * i);
+      copy16_to_lds(rk, copy_voff<D>(lane, i), base + 1024 * i);
+      copy16_to_lds(rv, copy_voff<D>(lane, i), base + kKVTileBytes + 1024 * i);
     }
   }
 
@@ -265,8 +296,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int nb = b_last - b_first + 1;  // blocks per query head
   const int n_items = group * nb;
   const int n_steps = (n_items + 1) / 2;
-  // group-local copy of item it into ring slot `slot`: Q and dO 8
-  // instructions each (2 per wave), then the LSE and D rows.
+  // group-local copy of item it into ring slot `slot`: Q and dO
+  // kQB / kRowsPerCopy instructions each, then the LSE and D rows.
   auto copy_block = [&](int it, int slot) __attribute__((always_inline)) {
     const int hq = bkv * group + it / nb;  // query head
     const int q0 = (b_first + it % nb) * kQB;
@@ -277,10 +308,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const unsigned base =
         __builtin_amdgcn_readfirstlane(lds_offset_of(lds_ring)) + (unsigned)((grp * 2 + slot) * kSlotBytes);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < kQB / Gm::kRowsPerCopy / 4; ++m) {
       const int i = gw + 4 * m;
-      copy16_to_lds(rq, copy_voff(lane, i), base + 1024 * i);
-      copy16_to_lds(rg, copy_voff(lane, i), base + kQBBytes + 1024 * i);
+      copy16_to_lds(rq, copy_voff<D>(lane, i), base + 1024 * i);
+      copy16_to_lds(rg, copy_voff<D>(lane, i), base + kQBBytes + 1024 * i);
     }
     if (gw < 2) {
       const float* src = (gw == 0 ? lse : delta) + (long long)hq * N + q0;
@@ -299,7 +330,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // transposing reads); slot 1 and the dO block are immediates on top.
   int krw[kKSteps], qrw[kKSteps], qtr[kDBlocks][2];
   {
-    const LdsOffsets off = lds_offsets(lane);
+    const LdsOffsets<D> off = lds_offsets<D>(lane);
     const int ring = 2 * kKVTileBytes + grp * 2 * kSlotBytes;
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) {
@@ -420,14 +451,14 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (s < n_steps) step(s, Sl0{});
 
   // ---- add the two groups' partial sums, then store ----
-  float* const red = (float*)smem;  // [wave 0..3][128 values][64 lanes]
+  float* const red = (float*)smem;  // [wave 0..3][kAccVals values][64 lanes]
   if (grp == 1) {
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        red[((gw * 128) + db * 16 + i) * 64 + lane] = dvacc[db][i];
-        red[((gw * 128) + 64 + db * 16 + i) * 64 + lane] = dkacc[db][i];
+        red[((gw * kAccVals) + db * 16 + i) * 64 + lane] = dvacc[db][i];
+        red[((gw * kAccVals) + kAccVals / 2 + db * 16 + i) * 64 + lane] = dkacc[db][i];
       }
   }
   __syncthreads();
@@ -436,8 +467,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      dvacc[db][i] += red[((gw * 128) + db * 16 + i) * 64 + lane];
-      dkacc[db][i] = (dkacc[db][i] + red[((gw * 128) + 64 + db * 16 + i) * 64 + lane]) * scale;
+      dvacc[db][i] += red[((gw * kAccVals) + db * 16 + i) * 64 + lane];
+      dkacc[db][i] = (dkacc[db][i] + red[((gw * kAccVals) + kAccVals / 2 + db * 16 + i) * 64 + lane]) * scale;
     }
   const long long krow = head + (long long)key * kD;
 #pragma unroll
@@ -462,16 +493,18 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 constexpr int kQWaves = kBwdQWaves;             // 8
 constexpr int kQRows = kBwdQRows;               // 256
 constexpr int kQCols = kBwdQCols;               // 64 keys per tile
-constexpr int kQTileBytes = kQCols * kRowBytes;  // 16 KiB (K or V)
-constexpr int kQStage = 2 * kQTileBytes;         // K then V
 constexpr int kQRing = 3;
 
-template <bool MASKED, bool GRAD_BF16>
+template <int D, bool MASKED, bool GRAD_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kQWaves * 64, kQWaves * 64), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                    const __bf16* __restrict__ dout, const float* __restrict__ lse,
                    const float* __restrict__ delta, void* __restrict__ dq, int BH, int N, int T, float c,
                    float scale, int group, int wl, int wr) {
+  using Gm = BG<D>;
+  constexpr int kD = D, kRowBytes = Gm::kRowBytes, kKSteps = Gm::kKSteps, kDBlocks = Gm::kDBlocks;
+  constexpr int kQTileBytes = kQCols * kRowBytes;  // K or V tile: 16 KiB at d = 128
+  constexpr int kQStage = 2 * kQTileBytes;         // K then V
   __shared__ __attribute__((aligned(1024))) char smem[kQRing * kQStage];
 
   const int lane = threadIdx.x & 63;
@@ -530,10 +563,10 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
   const int key_lo = (MASKED && wl >= 0) ? qrow - wl : 0;
   const int key_hi = (MASKED && wr >= 0) ? min(N - 1, qrow + wr) : N - 1;
 
-  const LdsOffsets off = lds_offsets(lane);
+  const LdsOffsets<D> off = lds_offsets<D>(lane);
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset_of(smem));
-  // tile copies: 16 instructions for K and 16 for V; instruction i is
-  // issued by wave i % 8
+  // tile copies: kQCols / kRowsPerCopy instructions for K and as many for V;
+  // instruction i is issued by wave i % 8
   auto copy_tile = [&](int j) __attribute__((always_inline)) {
     const int key0 = (j_lo + j) * kQCols;
     const int rows = min(kQCols, N - key0);
@@ -541,13 +574,13 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
     const i32x4 rv = raw_rsrc(v + kv_head + (long long)key0 * kD, rows * kRowBytes);
     const unsigned base = lds0 + (unsigned)((j % kQRing) * kQStage);
 #pragma unroll
-    for (int m = 0; m < kQCols / 4 / kQWaves; ++m) {
+    for (int m = 0; m < kQCols / Gm::kRowsPerCopy / kQWaves; ++m) {
       const int i = wave + kQWaves * m;
-      copy16_to_lds(rk, copy_voff(lane, i), base + 1024 * i);
-      copy16_to_lds(rv, copy_voff(lane, i), base + kQTileBytes + 1024 * i);
+      copy16_to_lds(rk, copy_voff<D>(lane, i), base + 1024 * i);
+      copy16_to_lds(rv, copy_voff<D>(lane, i), base + kQTileBytes + 1024 * i);
     }
   };
-  constexpr int kCopies = 2 * (kQCols / 4 / kQWaves);  // per wave per tile
+  constexpr int kCopies = 2 * (kQCols / Gm::kRowsPerCopy / kQWaves);  // per wave per tile
 
   f32x16 dqacc[kDBlocks];
 #pragma unroll
@@ -644,7 +677,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, c
     }
 }
 
-template <bool MASKED, bool GRAD_BF16>
+template <int D, bool MASKED, bool GRAD_BF16>
 hipError_t launch_bwd_t(const BwdArgs& a, float c) {
   const int BH = a.B * a.H;
   const int BHkv = a.B * a.Hkv;
@@ -653,35 +686,45 @@ hipError_t launch_bwd_t(const BwdArgs& a, float c) {
   const int T = (a.N + kQRows - 1) / kQRows;
   const long long q_grid = (long long)T * BH;
   if (kv_grid > 0x7fffffffLL || q_grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<MASKED, GRAD_BF16>), dim3((unsigned)kv_grid), dim3(kKVWaves * 64), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASKED, GRAD_BF16>), dim3((unsigned)kv_grid), dim3(kKVWaves * 64), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
                      a.delta, a.dk, a.dv, BHkv, a.N, c, a.scale, group, a.wl, a.wr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<MASKED, GRAD_BF16>), dim3((unsigned)q_grid), dim3(kQWaves * 64), 0, a.stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MASKED, GRAD_BF16>), dim3((unsigned)q_grid), dim3(kQWaves * 64), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
                      a.delta, a.dq, BH, a.N, T, c, a.scale, group, a.wl, a.wr);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_bwd_bf16(const BwdArgs& a) {
-  if (a.d != kD) return hipErrorInvalidValue;
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
-  const long long dgrid = (rows + 15) / 16;
+  constexpr int kRowsPerBlock = 256 / (D / 8);
+  const long long dgrid = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   if (dgrid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (a.o_bf16)
-    hipLaunchKernelGGL((bwd_delta_kernel<true>), dim3((unsigned)dgrid), dim3(256), 0, a.stream, a.o,
+    hipLaunchKernelGGL((bwd_delta_kernel<D, true>), dim3((unsigned)dgrid), dim3(256), 0, a.stream, a.o,
                        (const __bf16*)a.dout, a.delta, rows);
   else
-    hipLaunchKernelGGL((bwd_delta_kernel<false>), dim3((unsigned)dgrid), dim3(256), 0, a.stream, a.o,
+    hipLaunchKernelGGL((bwd_delta_kernel<D, false>), dim3((unsigned)dgrid), dim3(256), 0, a.stream, a.o,
                        (const __bf16*)a.dout, a.delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float c = fmaxf(a.scale * kLog2e, 1e-30f);
-  if (a.wl >= 0 || a.wr >= 0) return a.grad_bf16 ? launch_bwd_t<true, true>(a, c) : launch_bwd_t<true, false>(a, c);
-  return a.grad_bf16 ? launch_bwd_t<false, true>(a, c) : launch_bwd_t<false, false>(a, c);
+  if (a.wl >= 0 || a.wr >= 0)
+    return a.grad_bf16 ? launch_bwd_t<D, true, true>(a, c) : launch_bwd_t<D, true, false>(a, c);
+  return a.grad_bf16 ? launch_bwd_t<D, false, true>(a, c) : launch_bwd_t<D, false, false>(a, c);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  switch (a.d) {
+    case 64: return launch_bwd_d<64>(a);
+    case 128: return launch_bwd_d<128>(a);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fa2

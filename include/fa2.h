@@ -192,7 +192,7 @@ int fa2_fwd_window(const void* q, const void* k, const void* v, void* o, float* 
  *   o_dtype        FA2_F32 or FA2_BF16 (the dtype o was written in).
  *   grad_dtype     FA2_F32 or FA2_BF16 for dq, dk, dv (bf16: rounded to
  *                  nearest-even from the fp32 result).
- *   d              128 (others: FA2_ERR_UNSUPPORTED).
+ *   d              64 or 128 (others: FA2_ERR_UNSUPPORTED).
  *
  * Arithmetic: bf16 matrix-core products with fp32 accumulation; P and dS
  * are rounded to bf16 (nearest-even) before the products that consume them

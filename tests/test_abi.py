@@ -211,8 +211,8 @@ def _bcall(**over):
     (dict(dv=DK + 64), fa2.FA2_ERR_INVALID_ARG),    # outputs overlap each other
     (dict(delta=BL + 4), fa2.FA2_ERR_INVALID_ARG),  # workspace overlaps lse
     (dict(delta=DV + 16), fa2.FA2_ERR_INVALID_ARG),  # workspace overlaps an output
-    (dict(d=64), fa2.FA2_ERR_UNSUPPORTED),
     (dict(d=96), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(d=256), fa2.FA2_ERR_UNSUPPORTED),
     (dict(in_dtype=fa2.F32), fa2.FA2_ERR_UNSUPPORTED),
 ])
 def test_bwd_validation_rejects_before_any_hip_call(over, status):
@@ -300,9 +300,10 @@ def _wbcall(wl, wr, **over):
 def test_bwd_window_validation():
     assert _wbcall(-2, 0) == fa2.FA2_ERR_INVALID_ARG
     assert _wbcall(0, -7) == fa2.FA2_ERR_INVALID_ARG
-    assert _wbcall(5, 5, d=64) == fa2.FA2_ERR_UNSUPPORTED
+    assert _wbcall(5, 5, d=96) == fa2.FA2_ERR_UNSUPPORTED
     if not _gpu_present():
         assert _wbcall(5, 5) == fa2.FA2_ERR_NO_DEVICE
+        assert _wbcall(5, 5, d=64) == fa2.FA2_ERR_NO_DEVICE
         assert _wbcall(-1, 0) == fa2.FA2_ERR_NO_DEVICE
 
 

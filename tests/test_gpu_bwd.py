@@ -1,5 +1,5 @@
-"""GPU parity of the backward pass: the HIP path (through the C ABI) against
-the fp64 gradient oracle.
+"""GPU parity of the backward pass (d = 128 and d = 64): the HIP path
+(through the C ABI) against the fp64 gradient oracle.
 
 Bar (derived in the design notes from the arithmetic): bf16 inputs, P and dS
 rounded to bf16 (unit roundoff 2^-9 relative) before the products that use
@@ -217,3 +217,78 @@ def test_buffer_rejections_on_gpu():
         with pytest.raises(ValueError):
             fa2.backward(q, q, q, o, lse, g, **kw)
     torch.cuda.synchronize()
+
+
+# --- head dimension 64 ------------------------------------------------------
+# The same bar; d = 64 has its own LDS layout (rows of 128 bytes, two per
+# bank line, with their own chunk permutation) and copy geometry.
+
+SMALL64 = [
+    (1, 2, 127, True, False),
+    (2, 1, 300, False, True),
+    (1, 3, 520, True, True),
+    (1, 1, 33, True, False),
+    (1, 2, 1000, False, False),
+]
+
+
+def _inputs64(B, H, N, seed, outliers=False):
+    w = workloads.get("long_causal").with_(B=B, H=H, N=N, d=64, outlier_frac=0.001 if outliers else 0.0)
+    q, k, v = workloads.make_inputs(w, seed)
+    g = workloads.make_grad_output(w, seed + 7919)
+    return w, q, k, v, g
+
+
+@pytest.mark.parametrize("B,H,N,causal,outliers", SMALL64,
+                         ids=[f"d64-{b}x{h}x{n}-{'causal' if c else 'full'}{'-outl' if o else ''}"
+                              for b, h, n, c, o in SMALL64])
+def test_d64_every_element(B, H, N, causal, outliers):
+    w, q, k, v, g = _inputs64(B, H, N, seed=2000 + N, outliers=outliers)
+    scale = 0.125
+    print(f"[case] bwd d=64 B={B} H={H} N={N} causal={causal} outliers={outliers}", flush=True)
+    dq, dk, dv = _fwd_bwd(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), causal, scale)
+    Q, K, V, G = (_np64(t) for t in (q, k, v, g))
+    got = [_np64(t) for t in (dq, dk, dv)]
+    for b in range(B):
+        for h in range(H):
+            _check_head([x[b, h] for x in got], Q[b, h], K[b, h], V[b, h], G[b, h], scale, causal,
+                        f"d64 {B}x{H}x{N} causal={causal} head ({b},{h})")
+
+
+def test_d64_bf16_gradients_grouped_heads_and_window():
+    """d = 64 with bf16 gradients, 4 query heads on 2 key/value heads and a
+    window open on both sides, against the window oracle's group sums."""
+    B, H, Hkv, N, win = 1, 4, 2, 400, (70, 9)
+    w, q, k, v, g = _inputs64(B, H, N, seed=2101, outliers=True)
+    k, v = k[:, :Hkv].contiguous(), v[:, :Hkv].contiguous()
+    scale = 0.125
+    print(f"[case] bwd d=64 bf16 grads, {H}/{Hkv} heads, window {win}", flush=True)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa2.forward(qd, kd, vd, scale=scale, window=win)
+    got = fa2.backward(qd, kd, vd, o, lse, gd, scale=scale, window=win, grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Q, K, V, G = (_np64(t) for t in (q, k, v, g))
+    refs = gref.attention_grad_ref_window(Q, K, V, G, scale, *win)
+    mq, mk, mv = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for h in range(H):
+        gk = h // (H // Hkv)
+        a, bb, c = gref.grad_magnitudes_head_window(Q[0, h], K[0, gk], V[0, gk], G[0, h], scale, *win)
+        mq[0, h] = a
+        mk[0, gk] += bb
+        mv[0, gk] += c
+    for name, x, r, m in zip(("dQ", "dK", "dV"), got, refs, (mq, mk, mv)):
+        x = _np64(x)
+        bound = REL * m + 1e-6 * float(np.max(m)) + _bf16_half_ulp(r)
+        err = np.abs(x - r)
+        print(f"[bwd parity] d64 window {name}: max|err|={float(np.max(err)):.3e}", flush=True)
+        assert np.all(np.isfinite(x)) and np.all(err <= bound), name
+
+
+def test_d64_deterministic():
+    w, q, k, v, g = _inputs64(1, 2, 700, seed=2202, outliers=True)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    print("[case] bwd d=64 determinism", flush=True)
+    a = _fwd_bwd(qd, kd, vd, gd, True, 0.125)
+    b = _fwd_bwd(qd, kd, vd, gd, True, 0.125)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), "backward is not bitwise reproducible"
