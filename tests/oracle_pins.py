@@ -376,6 +376,31 @@ def pin_window_special_cases():
         _close(lse, lf, 1e-14, f"window ({wl},{wr}) vs full LSE")
 
 
+def pin_window_probabilities():
+    """probabilities_window (the probabilities the window gradients are built
+    from) on tiny random heads: each row equals exp(s_ij) / sum over the row's
+    band by explicit loops, is zero outside the band and sums to 1; the
+    window (-1, 0) gives the causal probabilities."""
+    rng = _rng(37)
+    for n, d, wl, wr in ((5, 3, 1, 1), (6, 2, -1, 2), (7, 4, 2, -1), (4, 2, 0, 0), (6, 3, 3, 1)):
+        q = rng.standard_normal((n, d))
+        k = rng.standard_normal((n, d))
+        scale = 0.7
+        p = ref.probabilities_window(q, k, scale, wl, wr)
+        for i in range(n):
+            band = [j for j in range(n) if (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)]
+            s = {j: scale * math.fsum(q[i, t] * k[j, t] for t in range(d)) for j in band}
+            den = math.fsum(math.exp(x) for x in s.values())
+            for j in range(n):
+                want = math.exp(s[j]) / den if j in s else 0.0
+                assert abs(p[i, j] - want) <= 1e-12, (n, wl, wr, i, j, p[i, j], want)
+            assert abs(math.fsum(p[i]) - 1.0) <= 1e-12
+    q = rng.standard_normal((9, 4))
+    k = rng.standard_normal((9, 4))
+    assert np.allclose(ref.probabilities_window(q, k, 0.5, -1, 0), ref.probabilities(q, k, 0.5, True),
+                       rtol=0, atol=1e-14)
+
+
 def pin_window_driver_grouped_heads():
     """The [B, H] sliding-window driver: 6 query heads on 3 key/value heads
     (query head h reads key/value head 0, 0, 1, 1, 2, 2) and on 1, two
@@ -581,6 +606,7 @@ PINS = [
     pin_block_sparse_layouts,
     pin_window_brute_force,
     pin_window_special_cases,
+    pin_window_probabilities,
     pin_window_driver_grouped_heads,
     pin_gqa_head_groups,
     pin_brute_force,

@@ -22,6 +22,23 @@ _orig_visible_window = ref.visible_window
 _orig_visible_bs = ref.visible_block_sparse
 _orig_gather = ref.gather_pages
 _orig_ref_window = ref.attention_ref_window
+_orig_probs_window = ref.probabilities_window
+
+
+def _probs_window_all_keys(q, k, scale, wl, wr):
+    # plausible mistake: the band masks the numerator but the sum runs over all keys
+    s = ref.scores(q, k, scale)
+    mask = ref.visible_window(np.arange(len(q)), np.arange(len(k)), wl, wr)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return np.where(mask, e, 0.0) / e.sum(axis=1, keepdims=True)
+
+
+def _probs_window_columns(q, k, scale, wl, wr):
+    # plausible mistake: normalised over the query axis
+    p = _orig_probs_window(q, k, scale, wl, wr)
+    num = p * _orig_probs_window(q, k, scale, wl, wr).sum(axis=1, keepdims=True)
+    return num / np.maximum(num.sum(axis=0, keepdims=True), 1e-300)
 
 
 def _window_driver_heads(head_of):
@@ -119,6 +136,8 @@ MUTANTS = {
     "window_driver_heads_ungrouped": ("attention_ref_window", _window_driver_heads(lambda h, n_h, n_kv: h)),
     "window_driver_heads_interleaved": ("attention_ref_window", _window_driver_heads(lambda h, n_h, n_kv: h % n_kv)),
     "window_driver_heads_clamped": ("attention_ref_window", _window_driver_heads(lambda h, n_h, n_kv: min(h, n_kv - 1))),
+    "window_probabilities_sum_over_all_keys": ("probabilities_window", _probs_window_all_keys),
+    "window_probabilities_over_queries": ("probabilities_window", _probs_window_columns),
 }
 
 
