@@ -383,3 +383,47 @@ def test_headline_whole_heads_every_row():
         print(f"[parity] {w.name} head ({b},{h}): all {w.N} rows", flush=True)
         eo, el = ref.attention_head(_np64(q[b, h]), _np64(k[b, h]), _np64(v[b, h]), w.scale, w.causal)
         _check(o[b, h], lse[b, h], eo, el, w.dtype, f"{w.name} head ({b},{h}) all rows")
+
+
+# --- a seeded random sweep ----------------------------------------------------
+# Shapes, masks (none, causal, windows on one or both sides), grouped heads
+# and O dtypes drawn from one seed; every element against the oracle.  The
+# draws are printed before each case runs.
+
+def _sweep_cases(n=18, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([64, 128]))
+        H_kv = int(rng.choice([1, 2, 4]))
+        H = H_kv * int(rng.choice([1, 2, 3]))
+        B = int(rng.integers(1, 4))
+        N = int(rng.integers(1, 1500))
+        kind = int(rng.integers(0, 4))
+        if kind == 0:
+            win = (-1, -1)
+        elif kind == 1:
+            win = (-1, 0)
+        elif kind == 2:
+            win = (int(rng.integers(0, 400)), int(rng.integers(-1, 60)))
+        else:
+            win = (-1, int(rng.integers(0, 300)))
+        cases.append((B, H, H_kv, N, d, win, bool(rng.integers(0, 2))))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("B,H,H_kv,N,d,win,o_bf16", SWEEP,
+                         ids=[f"{b}x{h}/{hk}x{n}x{d}-w{w[0]}_{w[1]}{'-bf16o' if ob else ''}"
+                              for b, h, hk, n, d, w, ob in SWEEP])
+def test_random_sweep_every_element(B, H, H_kv, N, d, win, o_bf16):
+    print(f"[case] sweep {B}x{H}/{H_kv}x{N}x{d} window {win} o {'bf16' if o_bf16 else 'fp32'}", flush=True)
+    q, k, v = _inputs(B, H, N, d, "bf16", seed=B * 1000 + H * 100 + N + d, outliers=0.001)
+    k, v = k[:, :H_kv].contiguous(), v[:, :H_kv].contiguous()
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa2.forward(q, k, v, scale=scale, window=win, o_dtype=torch.bfloat16 if o_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    eo, el = ref.attention_ref_window(_np64(q), _np64(k), _np64(v), scale, *win)
+    _check(o, lse, eo, el, "bf16", f"sweep {B}x{H}/{H_kv}x{N}x{d} window {win}", o_bf16=o_bf16)
