@@ -1425,8 +1425,23 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // wavefront (rows past N are dropped by the buffer range, not by a
   // branch), so that the next item can wait for its prefetch alone.
   constexpr int kStores = (kRows * D * (OUT_BF16 ? 2 : 4)) / 1024 + 1;  // 1 KiB of O per instruction, then LSE
+  // Issue priority falls with the workgroup's progress through its items:
+  // two workgroups share each CU, and the older one wins issue arbitration
+  // between equal priorities, so without this it runs ahead and the other
+  // finishes its items alone on a half-empty CU (measured: 10-15 us apart on
+  // short_seq, 59 us long).  A workgroup that falls a quarter of its items
+  // behind now takes precedence until it catches up.
+  const int n_rounds = !PERSIST ? 1 : sched == 1 ? (n_items - wg + n_wg - 1) / n_wg : (item_of(1) >= 0 ? 2 : 1);
   bool prefetched = false;
   for (int r = 0;; ++r) {
+    if (PERSIST) {
+      switch (min(3, 4 * r / n_rounds)) {
+        case 0: __builtin_amdgcn_s_setprio(3); break;
+        case 1: __builtin_amdgcn_s_setprio(2); break;
+        case 2: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
+      }
+    }
     enter();
 #pragma unroll
     for (int db = 0; db < G::kDBlocks; ++db)
