@@ -1167,14 +1167,15 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     __builtin_amdgcn_s_waitcnt(0xC07F);
   };
 
-  // ---- the next item, prefetched during the current item's last P V
-  // product: its K tiles 0 and 1 into K ring slots 0 and 1, its Q rows into
-  // qf.
-  bool pref = false;
+  // ---- the next item (nxt, or -1), prefetched during the current item's
+  // last P V product: its K tiles 0 and 1 into K ring slots 0 and 1, its Q
+  // rows into qf.  Only its index stays live through the tile loop (its
+  // geometry is recomputed where it is used): the looping kernel is short of
+  // scalar registers.
   int nxt = -1;
-  Item nx = cur;
   auto prefetch = [&]() __attribute__((always_inline)) {
-    if (pref) {
+    if (nxt >= 0) {
+      const Item nx = geom(nxt);
       const char* const kbase = (const char*)(k + (long long)(nx.bh / group) * N * D);
 #pragma unroll
       for (int kk = 0; kk < kCopyK; ++kk)
@@ -1433,7 +1434,10 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // behind now takes precedence until it catches up.
   const int n_rounds = !PERSIST ? 1 : sched == 1 ? (n_items - wg + n_wg - 1) / n_wg : (item_of(1) >= 0 ? 2 : 1);
   bool prefetched = false;
-  for (int r = 0;; ++r) {
+  // One item (the r-th of this workgroup); LAST: no item follows, so no
+  // prefetch.
+  auto item_body = [&](int r, auto last) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last)::value;
     if (PERSIST) {
       switch (min(3, 4 * r / n_rounds)) {
         case 0: __builtin_amdgcn_s_setprio(3); break;
@@ -1468,11 +1472,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     }
     __syncthreads();  // B_0: nobody reads K_0 any more
 
-    if (PERSIST) {
-      nxt = item_of(r + 1);
-      pref = nxt >= 0;
-      if (nxt >= 0) nx = geom(nxt);
-    }
+    if (PERSIST) nxt = LAST ? -1 : item_of(r + 1);
     // Tiles past tile 0 go in pairs (ring slots 1, 0); a lone last tile
     // computes no S and copies no K.  (When the last tile ends a pair it
     // computes an unused S and its K copy fetches the last tile again.)
@@ -1486,7 +1486,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     // the last O += V P: P_{n-1} with V_{n-1} (a stream "at tile n")
     {
       float d0, d1;
-      using CF = std::conditional_t<PERSIST, CP, C0>;
+      using CF = std::conditional_t<PERSIST && !LAST, CP, C0>;
       if (cur.n_tiles & 1) stream(cur.n_tiles, S1{}, sA, sB, T_{}, F_{}, F_{}, CF{}, d0, d1);
       else stream(cur.n_tiles, S0{}, sA, sB, T_{}, F_{}, F_{}, CF{}, d0, d1);
     }
@@ -1548,9 +1548,24 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (long long)cur.bh * N + min(qw, N), rows * 4);
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m * c + log2f(lt)) * 0.69314718055994531f), rl, l32 * 4,
                                           0, 0);
-    if (!PERSIST || nxt < 0) break;
-    prefetched = pref;
-    cur = nx;
+  };
+  if constexpr (PERSIST && D == 128) {
+    // At most two items per workgroup here (schedule 2, heaviest with
+    // lightest): the item body is inlined twice instead of looping, which
+    // leaves the register allocator no state to carry round a loop.
+    item_body(0, F_{});
+    if (nxt >= 0) {
+      prefetched = true;
+      cur = geom(nxt);
+      item_body(1, T_{});
+    }
+  } else {
+    for (int r = 0;; ++r) {
+      item_body(r, F_{});
+      if (!PERSIST || nxt < 0) break;
+      prefetched = true;
+      cur = geom(nxt);
+    }
   }
 }
 
