@@ -1607,6 +1607,8 @@ hipError_t launch_t(const FwdArgs& a) {
       const hipError_t eu = compute_units(&units);
       if (eu != hipSuccess) return eu;
       const FwdSchedule sc = fwd_schedule(items, units, MASKED && a.wl < 0, D);
+      // the d = 128 looping kernel runs at most two items per workgroup
+      if (D != 64 && (sc.sched == 1 || (sc.sched == 2 && 2 * sc.workgroups < items))) return hipErrorInvalidValue;
       auto kern = sc.sched == 0 ? fwd_kernel<D, MASKED, OUT_BF16, false> : fwd_kernel<D, MASKED, OUT_BF16, true>;
       hipLaunchKernelGGL(kern, dim3((unsigned)sc.workgroups), dim3(kThreads4), 0, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, a.B * a.H, a.N, T4, c, a.poison ? 1 : 0,
