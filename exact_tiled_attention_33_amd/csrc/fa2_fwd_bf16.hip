@@ -1241,7 +1241,8 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     // The softmax as a 3-stage pipeline over the 16 element pairs of a lane
     // (pair p: block p / 8, elements 2(p % 8) and +1).  Half-step 2u: exp2 of
     // pair u-1 and the exponent arguments of pair u; half-step 2u+1: sums
-    // and bf16 packing of pair u-2.  36 half-steps, spread over the MFMAs.
+    // and bf16 packing of pair u-2.  36 half-steps, spread over all MFMAs
+    // but the last four.
     float xs[2][2], es[2][2];  // [pair parity][element]
     float part[4] = {0.f, 0.f, 0.f, 0.f}, partb[2] = {0.f, 0.f};
     auto half_step = [&](int hs) __attribute__((always_inline)) {
@@ -1297,9 +1298,14 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
         snext[ns & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ns >> 1], ns < 2 ? f32x16{} : snext[ns & 1], 0, 0, 0);
       }
       if constexpr (SOFT) {
-        // half-steps hs with floor(hs * kNT / kHS) == n
+        // half-steps hs with floor(hs * kNTS / kHS) == n: spread over all
+        // but the last four MFMAs, under which the last exponentials finish
+        // before the tile's end reads their sums
+        constexpr int kNTS = kNT > 8 ? kNT - 4 : kNT;
+        if (n < kNTS) {
 #pragma unroll
-        for (int hs = (n * kHS + kNT - 1) / kNT; hs < ((n + 1) * kHS + kNT - 1) / kNT; ++hs) half_step(hs);
+          for (int hs = (n * kHS + kNTS - 1) / kNTS; hs < ((n + 1) * kHS + kNTS - 1) / kNTS; ++hs) half_step(hs);
+        }
       }
 #pragma unroll
       for (int cc = 0; cc < kNC; ++cc)
