@@ -1017,15 +1017,37 @@ __device__ __forceinline__ void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// K tiles of this kernel carry no pad inside their rows.  A copy
+// instruction fills 1 KiB of LDS: here kRowsPerInst whole rows i, i + kSuper,
+// i + 2 kSuper, ... of the tile (a "super-row"), followed by 16 unused bytes.
+// Row r then sits at (r % kSuper) * 1040 + (r / kSuper) * row bytes: 16
+// consecutive rows fall on 16 distinct 16-byte slots of a 256-byte bank
+// line (the score MFMA's b128 operand reads are conflict-free), rows r and
+// r + 32 are 512 bytes apart (a key block is an immediate offset), and a
+// tile is exactly kSuper instructions, none of them spent on pad bytes.
+template <int D>
+struct KRing {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowsPerInst = 1024 / kRowBytes;  // 4 (d = 128), 8 (d = 64)
+  static constexpr int kSuper = kBc / kRowsPerInst;      // copy instructions per tile
+  static constexpr int kSuperBytes = 1024 + 16;
+  static constexpr int kTile = kSuper * kSuperBytes;
+  static constexpr int kBytes = (kRing2 * kTile + 1023) / 1024 * 1024;  // keeps the V ring 1 KiB aligned
+  static constexpr int kBlock = (32 / kSuper) * kRowBytes;             // rows r -> r + 32
+  static_assert(kSuper % kFwdWaves == 0 && 32 % kSuper == 0 && kBlock == 512, "K ring shape");
+  static __device__ __forceinline__ int row_off(int r) { return (r % kSuper) * kSuperBytes + (r / kSuper) * kRowBytes; }
+};
+
 template <int D, bool MASKED, bool OUT_BF16, bool PERSIST>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads4, kThreads4), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                void* __restrict__ o, float* __restrict__ lse, int BH, int N, int T, float c, int poison, int group,
                int wl, int wr, int n_items, int sched) {
   using G = Geo<D, false>;
-  __shared__ __attribute__((aligned(1024))) char smem[kRing2 * (G::kTileK + G::kTileV)];
+  using KR = KRing<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[KR::kBytes + kRing2 * G::kTileV];
   char* const lds_k = smem;
-  char* const lds_v = smem + kRing2 * G::kTileK;
+  char* const lds_v = smem + KR::kBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1111,17 +1133,18 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // ---- copies: one instruction = 64 lanes x 16 bytes into 64 consecutive
   // 16-byte LDS slots; instruction i of a tile is issued by wavefront i % 4
   // (the layouts and per-lane source offsets are those of the other kernel)
-  constexpr int kCopyK = (G::kInstK + kW4 - 1) / kW4;
+  constexpr int kCopyK = KR::kSuper / kW4;
   constexpr int kCopyV = (G::kInstV + kW4 - 1) / kW4;
-  constexpr int kMainK = G::kInstK / kW4, kMainV = G::kInstV / kW4;
-  constexpr int kRemK = G::kInstK % kW4, kRemV = G::kInstV % kW4;
+  constexpr int kMainK = KR::kSuper / kW4, kMainV = G::kInstV / kW4;
+  constexpr int kRemK = 0, kRemV = G::kInstV % kW4;
   constexpr int kNC = kMainK + kMainV;  // copies spread through each tile's stream
   int voff_k[kCopyK], voff_v[kCopyV];
 #pragma unroll
   for (int kk = 0; kk < kCopyK; ++kk) {
     const int u = (wave + kk * kW4) * 64 + lane;
-    const int chunk = u % G::kSlotsK;
-    voff_k[kk] = (u / G::kSlotsK) * G::kRowBytes + (chunk < G::kChunks ? chunk : 0) * 16;
+    // instruction wave + 4 kk: rows (wave + 4 kk) + kSuper * (lane / chunks)
+    const int row = (wave + kk * kW4) + KR::kSuper * (lane / G::kChunks);
+    voff_k[kk] = row * G::kRowBytes + (lane % G::kChunks) * 16;
   }
 #pragma unroll
   for (int kk = 0; kk < kCopyV; ++kk) {
@@ -1129,7 +1152,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     const int row = u / G::kSlotsV, chunk = (u % G::kSlotsV) ^ (4 * G::vswz(row));
     voff_v[kk] = row * G::kRowBytes + chunk * 16;
   }
-  const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * 1024;
+  const unsigned lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_k)) + wave * KR::kSuperBytes;
   const unsigned lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset_of(lds_v)) + wave * 1024;
   // this wavefront's instruction kk of key tile jt (of the item whose keys
   // start at kbase, with tiles j_lo_ .. j_lo_ + n_tiles_ - 1) into ring slot
@@ -1141,7 +1164,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     const int rows = min(kBc, n_keys - key0);
     const unsigned long long gsrc = uniform_addr(kbase + (long long)key0 * G::kRowBytes);
     const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
-    copy16_to_lds(gsrc, min(voff_k[kk], lim), lds_k0 + slot * G::kTileK + kk * kW4 * 1024);
+    copy16_to_lds(gsrc, min(voff_k[kk], lim), lds_k0 + slot * KR::kTile + kk * kW4 * KR::kSuperBytes);
   };
   auto copy_k = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
     copy_k_of(kh, cur.j_lo, cur.n_tiles, jt, slot, kk);
@@ -1158,8 +1181,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     const u32x4 nan4 = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
     for (int kk = 0; kk < kCopyK; ++kk)
-      if (wave + kk * kW4 < G::kInstK)
-        *(__attribute__((address_space(3))) u32x4*)(size_t)(lds_k0 + kslot * G::kTileK + kk * kW4 * 1024 + 16 * lane) = nan4;
+      *(__attribute__((address_space(3))) u32x4*)(size_t)(lds_k0 + kslot * KR::kTile + kk * kW4 * KR::kSuperBytes + 16 * lane) = nan4;
 #pragma unroll
     for (int kk = 0; kk < kCopyV; ++kk)
       if (wave + kk * kW4 < G::kInstV)
@@ -1178,18 +1200,17 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
       const Item nx = geom(nxt);
       const char* const kbase = (const char*)(k + (long long)(nx.bh / group) * N * D);
 #pragma unroll
-      for (int kk = 0; kk < kCopyK; ++kk)
-        if (wave + kk * kW4 < G::kInstK) {
-          copy_k_of(kbase, nx.j_lo, nx.n_tiles, 0, 0, kk);
-          copy_k_of(kbase, nx.j_lo, nx.n_tiles, 1, 1, kk);
-        }
+      for (int kk = 0; kk < kCopyK; ++kk) {
+        copy_k_of(kbase, nx.j_lo, nx.n_tiles, 0, 0, kk);
+        copy_k_of(kbase, nx.j_lo, nx.n_tiles, 1, 1, kk);
+      }
       load_q((long long)nx.bh * N * D, nx.t * kBr4 + 32 * wave);
     }
   };
 
   // ---- LDS operand addresses: a per-lane base register plus an immediate
   // (ring slots are compile-time constants in the unrolled tile loop)
-  const int k_lane = (int)lds_offset_of(lds_k) + l32 * G::kStrideK + 16 * half;
+  const int k_lane = (int)lds_offset_of(lds_k) + KR::row_off(l32) + 16 * half;
   const int v_row = 4 * half + ((lane & 15) >> 2);
   const int v_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   int v_lane[G::kDBlocks];
@@ -1223,7 +1244,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     constexpr bool COPY_K = decltype(copy_kv)::value & 1, COPY_V = (decltype(copy_kv)::value & 2) != 0;
     constexpr bool PREF = (decltype(copy_kv)::value & 4) != 0;
     constexpr int kNT = (HAS_PV ? kNP : 0) + (HAS_S ? kNS : 0);
-    constexpr int kKOff = ((SL + 1) % kRing2) * G::kTileK;  // K_{j+1}
+    constexpr int kKOff = ((SL + 1) % kRing2) * KR::kTile;  // K_{j+1}
     constexpr int kVOff = ((SL + 1) % kRing2) * G::kTileV;  // V_{j-1}
     // A operand of stream MFMA n: for n < kNP (HAS_PV) V^T of key step
     // n / kDBlocks (keys 16*ks .. +15, transposing reads) for O^T block
@@ -1236,7 +1257,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       const int ns = n - (HAS_PV ? kNP : 0);
-      return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(k_lane + kKOff + 32 * (ns & 1) * G::kStrideK + 32 * (ns >> 1));
+      return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(k_lane + kKOff + KR::kBlock * (ns & 1) + 32 * (ns >> 1));
     };
     // The softmax as a 3-stage pipeline over the 16 element pairs of a lane
     // (pair p: block p / 8, elements 2(p % 8) and +1).  Half-step 2u: exp2 of
@@ -1408,7 +1429,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   auto copy_k_all = [&](int jt, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < kCopyK; ++kk)
-      if (wave + kk * kW4 < G::kInstK) copy_k(jt, slot, kk);
+      copy_k(jt, slot, kk);
   };
 
   // Key tile j (ring slot SL = j % 2; S_j in sA for even j, sB for odd).
