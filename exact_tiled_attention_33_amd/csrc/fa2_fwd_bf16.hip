@@ -1002,7 +1002,6 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // instruction then writes whole rows of O instead of 32-byte pieces of 32
 // rows, and exactly 1 KiB per instruction, so a wavefront issues a fixed
 // number of stores per item.
-constexpr int kRing2 = 2;               // K (and V) tiles resident per ring
 constexpr int kW4 = kFwdWaves;          // wavefronts per workgroup (one per SIMD)
 constexpr int kBr4 = kFwdBlockRows;     // query rows per workgroup
 constexpr int kThreads4 = kW4 * 64;
@@ -1025,14 +1024,14 @@ __device__ __forceinline__ void wait_vmem_n() {
 // line (the score MFMA's b128 operand reads are conflict-free), rows r and
 // r + 32 are 512 bytes apart (a key block is an immediate offset), and a
 // tile is exactly kSuper instructions, none of them spent on pad bytes.
-template <int D>
+template <int D, int R>
 struct KRing {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kRowsPerInst = 1024 / kRowBytes;  // 4 (d = 128), 8 (d = 64)
   static constexpr int kSuper = kBc / kRowsPerInst;      // copy instructions per tile
   static constexpr int kSuperBytes = 1024 + 16;
   static constexpr int kTile = kSuper * kSuperBytes;
-  static constexpr int kBytes = (kRing2 * kTile + 1023) / 1024 * 1024;  // keeps the V ring 1 KiB aligned
+  static constexpr int kBytes = (R * kTile + 1023) / 1024 * 1024;  // keeps the V ring 1 KiB aligned
   static constexpr int kBlock = (32 / kSuper) * kRowBytes;             // rows r -> r + 32
   static_assert(kSuper % kFwdWaves == 0 && 32 % kSuper == 0 && kBlock == 512, "K ring shape");
   static __device__ __forceinline__ int row_off(int r) { return (r % kSuper) * kSuperBytes + (r / kSuper) * kRowBytes; }
@@ -1044,8 +1043,14 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
                void* __restrict__ o, float* __restrict__ lse, int BH, int N, int T, float c, int poison, int group,
                int wl, int wr, int n_items, int sched) {
   using G = Geo<D, false>;
-  using KR = KRing<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[KR::kBytes + kRing2 * G::kTileV];
+  // Ring depth: at d = 128 two K and two V tiles (two workgroups per CU
+  // fill 130 KiB of LDS), and stream j copies K_{j+2} and V_j, each needed
+  // by stream j+1.  At d = 64 a stream is short, so a copy from HBM would
+  // not land within one stream: three of each, and stream j copies
+  // K_{j+3} and V_{j+1}, which have two streams to arrive.
+  constexpr int kR = D == 64 ? 3 : 2;
+  using KR = KRing<D, kR>;
+  __shared__ __attribute__((aligned(1024))) char smem[KR::kBytes + kR * G::kTileV];
   char* const lds_k = smem;
   char* const lds_v = smem + KR::kBytes;
 
@@ -1190,7 +1195,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   };
 
   // ---- the next item (nxt, or -1), prefetched during the current item's
-  // last P V product: its K tiles 0 and 1 into K ring slots 0 and 1, its Q
+  // last P V product: its K tiles 0 .. kR-1 into K ring slots 0 .. kR-1, its Q
   // rows into qf.  Only its index stays live through the tile loop (its
   // geometry is recomputed where it is used): the looping kernel is short of
   // scalar registers.
@@ -1203,6 +1208,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
       for (int kk = 0; kk < kCopyK; ++kk) {
         copy_k_of(kbase, nx.j_lo, nx.n_tiles, 0, 0, kk);
         copy_k_of(kbase, nx.j_lo, nx.n_tiles, 1, 1, kk);
+        if (kR == 3) copy_k_of(kbase, nx.j_lo, nx.n_tiles, 2, 2, kk);
       }
       load_q((long long)nx.bh * N * D, nx.t * kBr4 + 32 * wave);
     }
@@ -1244,20 +1250,41 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     constexpr bool COPY_K = decltype(copy_kv)::value & 1, COPY_V = (decltype(copy_kv)::value & 2) != 0;
     constexpr bool PREF = (decltype(copy_kv)::value & 4) != 0;
     constexpr int kNT = (HAS_PV ? kNP : 0) + (HAS_S ? kNS : 0);
-    constexpr int kKOff = ((SL + 1) % kRing2) * KR::kTile;  // K_{j+1}
-    constexpr int kVOff = ((SL + 1) % kRing2) * G::kTileV;  // V_{j-1}
+    // ring slots: tile t sits in slot t % kR (a compile-time SL-derived
+    // constant for kR = 2, uniform runtime values for kR = 3)
+    int kKOff = (kR == 2 ? (SL + 1) % 2 : (j + 1) % 3) * KR::kTile;  // K_{j+1}
+    int kVOff = (kR == 2 ? (SL + 1) % 2 : (j + 2) % 3) * G::kTileV;  // V_{j-1}
+    if constexpr (kR != 2) {
+      // whole offsets in scalar registers, so that each read base below
+      // takes one add (the compiler would split the modulo over several)
+      asm volatile("" : "+s"(kKOff));
+      asm volatile("" : "+s"(kVOff));
+    }
+    const int kSlotW = kR == 2 ? SL : j % 3;                                // K_{j+kR}
+    const int vSlotW = kR == 2 ? SL : (j + 1) % 3;                          // V_{j+kR-2}
+    // per-lane read bases of this stream's slots, formed once (with runtime
+    // slots the compiler would otherwise add the slot offset at every read)
+    int k_base = k_lane + kKOff;
+    int v_base[G::kDBlocks];
+#pragma unroll
+    for (int db = 0; db < G::kDBlocks; ++db) v_base[db] = v_lane[db] + kVOff;
+    if constexpr (kR != 2) {
+      asm volatile("" : "+v"(k_base));
+#pragma unroll
+      for (int db = 0; db < G::kDBlocks; ++db) asm volatile("" : "+v"(v_base[db]));
+    }
     // A operand of stream MFMA n: for n < kNP (HAS_PV) V^T of key step
     // n / kDBlocks (keys 16*ks .. +15, transposing reads) for O^T block
     // n % kDBlocks; then K rows 32*(ns & 1) .. +31 at k-step ns / 2
     auto read_op = [&](int n) __attribute__((always_inline)) {
       if (HAS_PV && n < kNP) {
         const int db = n % G::kDBlocks, ks = n / G::kDBlocks, kb = ks >> 1, h = ks & 1;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(v_lane[db] + kVOff + (32 * kb + 16 * h) * G::kStrideV));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(v_lane[db] + kVOff + (32 * kb + 16 * h + 8) * G::kStrideV));
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(v_base[db] + (32 * kb + 16 * h) * G::kStrideV));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(v_base[db] + (32 * kb + 16 * h + 8) * G::kStrideV));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       const int ns = n - (HAS_PV ? kNP : 0);
-      return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(k_lane + kKOff + KR::kBlock * (ns & 1) + 32 * (ns >> 1));
+      return *(const __attribute__((address_space(3))) bf16x8*)(size_t)(k_base + KR::kBlock * (ns & 1) + 32 * (ns >> 1));
     };
     // The softmax as a 3-stage pipeline over the 16 element pairs of a lane
     // (pair p: block p / 8, elements 2(p % 8) and +1).  Half-step 2u: exp2 of
@@ -1332,9 +1359,9 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
       for (int cc = 0; cc < kNC; ++cc)
         if (n == (kNT * cc) / (2 * kNC)) {
           if (cc < kMainK) {
-            if constexpr (COPY_K) copy_k(j + 2, SL, cc);
+            if constexpr (COPY_K) copy_k(j + kR, kSlotW, cc);
           } else {
-            if constexpr (COPY_V) copy_v(j, SL, cc - kMainK);
+            if constexpr (COPY_V) copy_v(j + kR - 2, vSlotW, cc - kMainK);
           }
         }
       if constexpr (PREF) {
@@ -1425,27 +1452,40 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   using CP = std::integral_constant<int, 4>;   // the next item's prefetch
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  // all of this wavefront's copy instructions of K tile jt
+  // all of this wavefront's copy instructions of K (V) tile jt
   auto copy_k_all = [&](int jt, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < kCopyK; ++kk)
       copy_k(jt, slot, kk);
   };
+  auto copy_v_all = [&](int jt, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < kCopyV; ++kk)
+      if (wave + kk * kW4 < G::kInstV) copy_v(jt, slot, kk);
+  };
 
-  // Key tile j (ring slot SL = j % 2; S_j in sA for even j, sB for odd).
+  // Key tile j (SL = j % 2: S_j in sA for even j, sB for odd; ring slots
+  // j % kR).
   auto tile = [&](int j, auto slot, auto has_pv, auto has_s, auto cp) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
-    constexpr bool COPY_K = decltype(cp)::value & 1;
+    constexpr bool COPY_K = decltype(cp)::value & 1, COPY_V = (decltype(cp)::value & 2) != 0;
     f32x16 (&scur)[2] = SL ? sB : sA;
     f32x16 (&snext)[2] = SL ? sA : sB;
-    if (poison) poison_slots(SL, SL);
-    if (COPY_K && kRemK > 0 && wave < kRemK) copy_k(j + 2, SL, kMainK);
-    if (kRemV > 0 && wave < kRemV) copy_v(j, SL, kMainV);
+    const int kSlotW = kR == 2 ? SL : j % 3, vSlotW = kR == 2 ? SL : (j + 1) % 3;
+    if (poison) poison_slots(kSlotW, vSlotW);
+    if (COPY_K && kRemK > 0 && wave < kRemK) copy_k(j + kR, kSlotW, kMainK);
+    if (COPY_V && kRemV > 0 && wave < kRemV) copy_v(j + kR - 2, vSlotW, kMainV);
     mask_tile(j, scur);  // diagonal / window edges, and the ragged last tile
     float tt, tb;
     stream(j, slot, scur, snext, has_pv, has_s, T_{}, cp, tt, tb);
     settle(scur, tt, tb);
-    wait_vmem(0);
+    if constexpr (kR == 2) {
+      wait_vmem(0);
+    } else {
+      // this stream's copies may stay in flight (next needed two streams
+      // on); the previous stream's, which the next one reads, must be in
+      wait_vmem_n<(COPY_K ? kMainK : 0) + (COPY_V ? kMainV : 0)>();
+    }
     __syncthreads();  // B_{j+1}
   };
 
@@ -1488,11 +1528,15 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
       load_q(head, qw);
       copy_k_all(0, 0);
       copy_k_all(1, 1);
+      if (kR == 3) copy_k_all(2, 2);
       wait_vmem(0);
     } else {
       wait_vmem_n<kStores>();  // the prefetch, not the previous item's stores
     }
     __syncthreads();
+    // kR = 3: V_0 (needed two streams on), issued after the barrier since the
+    // previous item staged its O in this part of the V ring
+    if (kR == 3) copy_v_all(0, 0);
     {
       float d0, d1;
       stream(-1, S1{}, sB, sA, F_{}, T_{}, F_{}, C0{}, d0, d1);  // "tile -1": S_0 (slot 0) into sA
@@ -1509,7 +1553,11 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
       tile(j, S1{}, T_{}, T_{}, CKV{});
       tile(j + 1, S0{}, T_{}, T_{}, CKV{});
     }
-    if (j < cur.n_tiles) tile(j, S1{}, T_{}, F_{}, CV{});
+    if (j < cur.n_tiles) {
+      // (kR = 3: the V tile this one would copy lies past the last)
+      using CL = std::conditional_t<kR == 2, CV, C0>;
+      tile(j, S1{}, T_{}, F_{}, CL{});
+    }
     // the last O += V P: P_{n-1} with V_{n-1} (a stream "at tile n")
     {
       float d0, d1;
@@ -1534,7 +1582,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     // past its last P V product: the barrier below); rows of kStageCols
     // columns, their 16-byte units XOR-permuted by the row so that the
     // column-wise writes of the 32 rows spread over the banks.
-    constexpr int kStageBytes = kRing2 * G::kTileV / kW4;          // per wave
+    constexpr int kStageBytes = 2 * G::kTileV / kW4;               // per wave (V slots 0 and 1)
     constexpr int kStageCols = kStageBytes / (kRows * kEsz);        // columns per pass
     constexpr int kPasses = D / kStageCols;
     constexpr int kUnits = kStageCols * kEsz / 16;                  // 16-byte units per staged row
