@@ -169,6 +169,11 @@ SCHED_EQUAL = [
     (4, 37, 1000),   # 1,184 items: three rounds, the last one short; B*H not a multiple of 8
     (8, 16, 600),    # 640 items, B*H a multiple of 8 (XCD-major order)
     (3, 50, 513),    # 750 items, one row past a tile edge
+    # items of 1, 2 and 3 key tiles: the ring's first slots, the clamped
+    # copies past the last tile and the next item's prefetch all meet
+    (9, 64, 64),     # 576 items of one key tile
+    (5, 128, 100),   # 640 items of two key tiles, the second ragged
+    (2, 160, 190),   # 640 items of three key tiles (two query tiles per head)
 ]
 
 
@@ -345,7 +350,10 @@ def test_buffer_rejections_on_gpu():
 # ordinary run.
 
 POISON_CASES = [(1, 2, 1000, 64, True), (2, 3, 777, 128, False), (1, 4, 1024, 128, True),
-                (2, 4, 600, 64, False), (1, 8, 700, 128, False)]
+                (2, 4, 600, 64, False), (1, 8, 700, 128, False),
+                # d = 64 grids of more than two items per CU: rounds of items with
+                # the next item's prefetch, items of 1, 3 and 16 key tiles
+                (9, 64, 64, 64, False), (2, 160, 190, 64, False), (4, 37, 1000, 64, False)]
 
 
 @pytest.mark.parametrize("B,H,N,d,causal", POISON_CASES,
