@@ -149,6 +149,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// cache policy of a buffer access: non-temporal (gfx950's nt bit)
+constexpr int kCpolNT = 2;
+
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
@@ -1616,7 +1619,9 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
         const int row = rd * kRowsPerRead + lane / kUnits, unit = lane % kUnits;
         const u32x4 y = *(const __attribute__((address_space(3))) u32x4*)(size_t)lds_offset_of(
             stage + row * (kStageCols * kEsz) + (unit ^ (row % kUnits)) * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(y, ro, row * (D * kEsz) + ps * (kStageCols * kEsz) + unit * 16, 0, 0);
+        // non-temporal: O is not read again here, and streaming it past the
+        // caches leaves them to the K and V tiles other workgroups still read
+        __builtin_amdgcn_raw_buffer_store_b128(y, ro, row * (D * kEsz) + ps * (kStageCols * kEsz) + unit * 16, 0, kCpolNT);
       }
     }
     // both halves of a row hold the same LSE; both store it
