@@ -982,11 +982,12 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // that only issues MFMAs starves the VALU instructions of the other
 // wavefront of its SIMD, so the overlap has to happen inside each stream.
 //
-// K and V tiles of 64 keys live in 2-deep LDS rings (slot = tile % 2).  The
-// stream of tile j copies K_{j+2} and V_j (global -> LDS, spread over its
-// first MFMAs) into the slots of K_j and V_{j-2}, which nobody reads after
-// the barrier that starts tile j; the barrier at the end of tile j, after
-// each wavefront's wait for its own copies, publishes them.
+// K and V tiles of 64 keys live in LDS rings of kR slots (slot = tile % kR;
+// kR = 2 at d = 128, 3 at d = 64).  The stream of tile j copies K_{j+kR}
+// and V_{j+kR-2} (global -> LDS, spread over its first MFMAs) into the
+// slots of K_j and V_{j-2}, which nobody reads after the barrier that
+// starts tile j; the barrier at the end of tile j, after each wavefront's
+// wait for the copies the next stream reads, publishes them.
 //
 // A workgroup may own several (query tile, batch*head) items in turn
 // (`sched`): 0 = one item, blockIdx.x; 1 = items g, g + G, g + 2G, ... (G
@@ -997,7 +998,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 // heaviest-first order (items g and 2G-1-g, then 2G+g, ...), which pairs
 // long causal items with short ones into equal loads when there are at
 // most two per workgroup slot.  The last P V product of an item reads no
-// K, so its stream copies the next item's first two K tiles into the K ring
+// K, so its stream copies the next item's first kR K tiles into the K ring
 // and loads the next item's Q rows: those loads are in flight while the
 // item finishes and stores O, and the next item waits for them alone.
 //
@@ -1241,7 +1242,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // One key tile's stream.  HAS_PV: O^T += V_{j-1}^T P_{j-1}^T;  HAS_S:
   // snext = K_{j+1} Q^T;  SOFT: P_j = exp2(S_j*c - m*c) from scur into pk,
   // with the row sums of the fp32 and of the bf16-rounded P;  copy_kv: bit 0
-  // K_{j+2}, bit 1 V_j, bit 2 the next item's prefetch (at the first MFMA).
+  // K_{j+kR}, bit 1 V_{j+kR-2}, bit 2 the next item's prefetch (at the first MFMA).
   // The sched_barrier after every MFMA and the empty asm statements that use
   // each softmax step's results keep the interleave the source order states
   // (the compiler would otherwise gather the VALU work).
@@ -1499,8 +1500,8 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // Issue priority falls with the workgroup's progress through its items:
   // two workgroups share each CU, and the older one wins issue arbitration
   // between equal priorities, so without this it runs ahead and the other
-  // finishes its items alone on a half-empty CU (measured: 10-15 us apart on
-  // short_seq, 59 us long).  A workgroup that falls a quarter of its items
+  // finishes its items alone on a half-empty CU (measured: 10-15 us apart in
+  // a 59 us run of [32, 16, 512, 64] at d = 64).  A workgroup that falls a quarter of its items
   // behind now takes precedence until it catches up.
   const int n_rounds = !PERSIST ? 1 : sched == 1 ? (n_items - wg + n_wg - 1) / n_wg : (item_of(1) >= 0 ? 2 : 1);
   bool prefetched = false;
@@ -1526,7 +1527,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     m_set = false;
     l = 0.f;
     lb = 0.f;
-    // ---- prologue: K_0 and K_1 in LDS, S_0 computed
+    // ---- prologue: K_0 .. K_{kR-1} (and, for kR = 3, V_0) in LDS, S_0 computed
     if (!prefetched) {
       load_q(head, qw);
       copy_k_all(0, 0);
