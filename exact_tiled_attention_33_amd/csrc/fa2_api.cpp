@@ -458,13 +458,20 @@ int fa2_decode_paged_workspace(int B, int H, int H_kv, int n_q, int d, int max_c
   const int bc = fa2::kBf16BlockCols;
   if (split_keys < 0 || split_keys % bc != 0) return FA2_ERR_INVALID_ARG;
   if (split_keys == 0) {
-    // enough chunks for about eight workgroups per compute unit at the
-    // longest context (shorter sequences have fewer, so about four on
-    // average for a mixed batch), at least four key tiles per chunk unless
-    // the context is shorter
+    // At least four key tiles per chunk unless the context is shorter, and:
+    // - groups of up to 32 query rows run one wavefront per (chunk, group),
+    //   four per compute unit: enough chunks at the longest context for one
+    //   chunk per wavefront slot (more chunks start a second, partial round;
+    //   fewer leave slots idle), or four per sequence once the groups alone
+    //   fill the slots (smaller chunks balance the rounds);
+    // - larger groups run workgroups of the forward kernel: about eight per
+    //   compute unit at the longest context (about four on average for a
+    //   mixed batch).
     if (num_units < 1) return FA2_ERR_INVALID_ARG;
     const long long groups = (long long)B * H_kv;
-    const long long want = std::max<long long>(1, (8LL * num_units + groups - 1) / groups);
+    const long long slots = (long long)(H / H_kv) * n_q <= 32 ? 4LL * num_units : 0;
+    const long long want = slots > 0 ? (groups < slots ? (slots + groups - 1) / groups : 4)
+                                     : std::max<long long>(1, (8LL * num_units + groups - 1) / groups);
     long long keys = (max_context + want - 1) / want;
     keys = (keys + bc - 1) / bc * bc;
     const long long floor_keys = std::min<long long>(4 * bc, ((long long)max_context + bc - 1) / bc * bc);

@@ -105,6 +105,18 @@ __device__ __forceinline__ void dec_copy16(unsigned long long base, int voff, un
 }
 #pragma clang diagnostic pop
 
+// Waits for a loaded value before the next tile copy is issued.  The
+// compiler cannot see the copies (inline asm), so to it a register load
+// stays the newest vector-memory operation: a use of it inside the tile
+// loop would get a vmcnt(0) wait, which in hardware also drains the tile
+// in flight -- on every tile.  Using the value here, in an asm statement
+// that stays ordered before the copies and redefines it, puts that wait
+// once before the copies instead.
+template <typename T>
+__device__ __forceinline__ void dec_landed(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 __device__ __forceinline__ unsigned long long dec_uniform(const void* p) {
   const unsigned long long b = reinterpret_cast<unsigned long long>(p);
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(b & 0xffffffffu));
@@ -170,11 +182,30 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_wave_kernel(const __bf1
   const char* const lds_wave_ptr = smem + w * G::kWaveLds;
   const int row_bytes = pg.kv_heads * G::kRowBytes;  // bytes between consecutive keys in the cache
 
+  // The chunk's page numbers, one per lane for 64 pages at a time: a tile
+  // takes its page with a lane read, not a load.  Tiles never straddle
+  // pages (pages hold a multiple of 64 keys), so the page number grows by
+  // at most one per tile and a new window is loaded once per 64 pages.
+  int page_base = key_begin / pg.page_size;
+  int page_lane = page_row[min(page_base + lane, pg.max_pages - 1)];
+  auto page_of = [&](int key0) __attribute__((always_inline)) {
+    const int pi = key0 / pg.page_size;
+    if (pi - page_base >= 64) {
+      page_base += 64;
+      page_lane = page_row[min(page_base + lane, pg.max_pages - 1)];
+      dec_landed(page_lane);
+    }
+    return min(max(__builtin_amdgcn_readlane(page_lane, pi - page_base), 0), pg.n_pages - 1);
+  };
+  dec_landed(page_lane);
+#pragma unroll
+  for (int s = 0; s < G::kKSteps; ++s) dec_landed(qf[s]);
+
   // Copy tile i (keys key0 .. key0 + 31 of this chunk) into stage st.
   auto copy_tile = [&](int i, int st) __attribute__((always_inline)) {
     const int key0 = (t0 + i) * kDecKeys;
     const int rows = min(kDecKeys, n_keys - key0);
-    const int page = min(max(page_row[key0 / pg.page_size], 0), pg.n_pages - 1);
+    const int page = page_of(key0);
     const long long off = (((long long)page * pg.page_size + key0 % pg.page_size) * pg.kv_heads + kvh) * D;
     const unsigned long long gk = dec_uniform(kc + off), gv = dec_uniform(vc + off);
     const unsigned base = lds_wave + st * G::kStage;

@@ -8,8 +8,18 @@ import exact_tiled_attention_33_amd as fa2
 
 
 def test_workspace_helper():
-    # 256 groups on 256 units: eight chunks of 1024 keys for an 8192-key context
-    assert fa2.fa2_decode_paged_workspace(32, 32, 8, 1, 128, 8192, 0, 256) == (1024, 32 * 8 * 8 * 4 * 1 * (128 * 4 + 8))
+    # groups of 4 rows (one wavefront per chunk): 256 groups on 256 units:
+    # 1024 wavefront slots, four chunks of 2048 keys for an 8192-key context
+    assert fa2.fa2_decode_paged_workspace(32, 32, 8, 1, 128, 8192, 0, 256) == (2048, 32 * 8 * 4 * 4 * 1 * (128 * 4 + 8))
+    # 512 groups: two chunks of 4096 keys; 16 x 8 = 128 groups: eight of 1024
+    assert fa2.fa2_decode_paged_workspace(64, 32, 8, 1, 128, 8192, 0, 256)[0] == 4096
+    assert fa2.fa2_decode_paged_workspace(16, 32, 8, 1, 128, 8192, 0, 256)[0] == 1024
+    # the groups alone fill the slots: four chunks per sequence
+    assert fa2.fa2_decode_paged_workspace(256, 32, 8, 1, 128, 8192, 0, 256)[0] == 2048
+    # groups of 64 rows (forward kernel workgroups): about eight per unit, at
+    # least 256 keys per chunk
+    assert fa2.fa2_decode_paged_workspace(4, 64, 1, 1, 128, 8192, 0, 256)[0] == 256
+    assert fa2.fa2_decode_paged_workspace(1, 64, 1, 1, 128, 1 << 20, 0, 256)[0] == 512
     # a short context: one chunk covering it
     sk, ws = fa2.fa2_decode_paged_workspace(1, 8, 1, 1, 128, 100, 0, 256)
     assert sk == 128 and ws == 1 * 1 * 1 * 8 * (128 * 4 + 8)

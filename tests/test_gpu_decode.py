@@ -46,6 +46,9 @@ CASES = [
     (2, 8, 8, 2, 128, 64, [0, 130], 128, True),
     (1, 64, 1, 4, 64, 64, [300], 64, False),
     (2, 8, 1, 3, 128, 128, [129, 2], 0, True),
+    # chunks of more than 64 pages: the page numbers are read 64 at a time
+    (2, 8, 2, 1, 128, 64, [6000, 8191], 8192, False),
+    (1, 4, 1, 2, 64, 64, [9000], 4160, False),
 ]
 
 
