@@ -1593,6 +1593,15 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     constexpr int kRowsPerRead = 64 / kUnits;                       // rows per 64-lane read
     static_assert(kStageCols % 32 == 0 && D % kStageCols == 0 && kUnits <= 64 && 64 % kUnits == 0, "stage shape");
     char* const stage = lds_v + wave * kStageBytes;
+    if constexpr (kR == 3) {
+      // A last tile that ends a pair (an odd tile count) copied the last V
+      // tile again into V slot n_tiles % 3, which may be part of the stage,
+      // and the tile-end wait left that copy in flight: it must land before
+      // the stage is written.  Only the next item's K and Q loads, issued
+      // after it, may stay in flight.
+      if (PERSIST && !LAST && nxt >= 0) wait_vmem_n<kR * kCopyK>();
+      else wait_vmem_n<0>();
+    }
     __syncthreads();  // every wave's last P V product has read the V ring
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {

@@ -174,6 +174,10 @@ SCHED_EQUAL = [
     (9, 64, 64),     # 576 items of one key tile
     (5, 128, 100),   # 640 items of two key tiles, the second ragged
     (2, 160, 190),   # 640 items of three key tiles (two query tiles per head)
+    # an odd tile count ends on a tile pair, whose clamped V copy lands in
+    # ring slot n % 3: 0 or 1 is where the O stage goes (7 and 3 tiles)
+    (2, 96, 448),    # 768 items of seven key tiles
+    (6, 120, 180),   # 1,440 items of three key tiles, the third ragged
 ]
 
 
