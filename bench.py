@@ -159,16 +159,17 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch from profiles/<kernel>_<workload>_hbm.md, if it
-    was measured on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"fa2_fwd_{workload}_hbm.md")
+def traffic_from_profiles(workload: str, profile: str = None, sources=None):
+    """HBM bytes per launch of the dominant kernel from profiles/<profile>_hbm.md
+    (profile defaults to fa2_fwd_<workload>), if it was measured on the
+    current sources of that kernel (default: the forward's); else None."""
+    path = os.path.join(ROOT, "profiles", f"{profile or 'fa2_fwd_' + workload}_hbm.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
 
@@ -380,14 +381,15 @@ def run_bench(args) -> dict:
         peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
         fp8_timing = {"step_ms_avg": round(step_ms, 4), "attention_kernel_ms_avg": round(avg_launch_ms, 4),
                       "pack_ms_avg": round(step_ms - avg_launch_ms, 4)}
+    # the counter summaries are taken on the plain forward with fp32 O
     plain_run = (hkv == w.H and args.window is None and not schedule["split"] and sparse_pairs is None
-                 and fp8_kernel is None)
+                 and fp8_kernel is None and args.o_dtype == "fp32")
     traffic = traffic_from_profiles(w.name) if plain_run else None
     prof = os.path.join("profiles", f"fa2_fwd_{w.name}_hbm.md")
     if traffic is not None:
         traffic_source = prof
     elif not plain_run:
-        traffic_source = "none: counters are taken for the plain forward of the workload only"
+        traffic_source = "none: counters are taken for the plain forward of the workload (fp32 O) only"
     elif not os.path.exists(os.path.join(ROOT, prof)):
         traffic_source = f"none: no {prof}"
     else:
@@ -664,6 +666,18 @@ def run_bench_decode(args) -> dict:
     alg_bytes = kv_bytes + rows * cfg["d"] * 2 + rows * cfg["d"] * (2 if args.o_dtype == "bf16" else 4) + rows * 4
     flops = 4.0 * cfg["H"] * cfg["d"] * sum(lens) * cfg["n_q"]
     gbs = alg_bytes / (avg_ms * 1e-3) / 1e9
+    # counters are taken on this batch with the library's chunk and fp32 O
+    prof = os.path.join("profiles", "fa2_decode_paged_hbm.md")
+    counted_run = args.split_keys == 0 and args.o_dtype == "fp32" and args.seed == 0
+    traffic = traffic_from_profiles("paged_decode", "fa2_decode_paged", DECODE_SOURCES) if counted_run else None
+    if traffic is not None:
+        traffic_source = prof
+    elif not counted_run:
+        traffic_source = "none: counters are taken for the default batch, chunk and fp32 O only"
+    elif not os.path.exists(os.path.join(ROOT, prof)):
+        traffic_source = f"none: no {prof}"
+    else:
+        traffic_source = f"none: the kernel sources changed since {prof} was measured"
     return {
         "metric": METRIC_DECODE,
         "value": round(alg_bytes * args.steps / wall / 1e9, 1),
@@ -674,7 +688,8 @@ def run_bench_decode(args) -> dict:
         "config": {"workload": "paged_decode", **cfg, "context_lens_sum": sum(lens), "max_context": max_ctx,
                    "split_keys": split, "o_dtype": args.o_dtype, "seed": args.seed, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel_ms_avg": round(avg_ms, 4),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, "traffic_source": traffic_source,
+                     "kernel_ms_avg": round(avg_ms, 4),
                      "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops,
                      "arithmetic_intensity": round(flops / alg_bytes, 2)},
         "timing": {"per_launch_ms_min": round(min(per_launch_ms), 4),
