@@ -560,6 +560,18 @@ def run_bench_bwd(args) -> dict:
     executed = 14.0 * w.B * w.H * w.d * pairs
     value = flops * args.steps / wall / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
+    # counters are taken per call (the three kernels) on the plain causal workload
+    prof = os.path.join("profiles", f"fa2_bwd_{w.name}_hbm.md")
+    counted_run = hkv == w.H and args.window is None
+    traffic = traffic_from_profiles(w.name, f"fa2_bwd_{w.name}", BWD_SOURCES) if counted_run else None
+    if traffic is not None:
+        traffic_source = prof
+    elif not counted_run:
+        traffic_source = "none: counters are taken for the plain workload only"
+    elif not os.path.exists(os.path.join(ROOT, prof)):
+        traffic_source = f"none: no {prof}"
+    else:
+        traffic_source = f"none: the kernel sources changed since {prof} was measured"
     result = {
         "metric": METRIC_BWD,
         "value": round(value, 2),
@@ -587,7 +599,8 @@ def run_bench_bwd(args) -> dict:
             "peak": round(PEAK_BF16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_source": traffic_source,
             "scope": "one fa2_bwd call (D, dK/dV and dQ kernels), HIP events on its stream",
             "call_ms_avg": round(avg_ms, 4),
             "algorithmic_flops_per_call": flops,
