@@ -1041,11 +1041,13 @@ struct KRing {
   static __device__ __forceinline__ int row_off(int r) { return (r % kSuper) * kSuperBytes + (r / kSuper) * kRowBytes; }
 };
 
-template <int D, bool MASKED, bool OUT_BF16, bool PERSIST>
+template <int D, bool MASKED, bool OUT_BF16, bool PERSIST, bool SPARSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads4, kThreads4), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                void* __restrict__ o, float* __restrict__ lse, int BH, int N, int T, float c, int poison, int group,
-               int wl, int wr, int n_items, int sched) {
+               int wl, int wr, int n_items, int sched, const int* __restrict__ sp_ptr,
+               const unsigned* __restrict__ sp_ent, int n_layouts, int n_entries) {
+  static_assert(!(SPARSE && PERSIST), "block-sparse items run one per workgroup");
   using G = Geo<D, false>;
   // Ring depth: at d = 128 two K and two V tiles (two workgroups per CU
   // fill 130 KiB of LDS), and stream j copies K_{j+2} and V_j, each needed
@@ -1113,6 +1115,63 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   int item = item_of(0);
   if (item < 0) return;
   Item cur = geom(item);
+
+  // Block-sparse: the item's key tiles are the entries of its 256-row
+  // tile's list (entry = key tile | slice bits << 24, bit s set when the
+  // rows 32s .. 32s+31 of the 256-row tile see that key tile) whose four
+  // slice bits of this 128-row half are not all clear, in the list's order.
+  // They are compacted once, through a scratch in V ring slot 1 (first
+  // written by a copy after the item's first barrier), into one lane
+  // register of 16-bit entries (key tile | the half's four slice bits << 8):
+  // entry i in bits 16*(i / 64) of lane i % 64.  At most 128 (the host takes
+  // this kernel only while N <= 8192, so key tiles fit 8 bits).
+  unsigned sp_list = 0u;
+  int sp_bit = 0;  // this wavefront's slice bit in an entry
+  if constexpr (SPARSE) {
+    const int T2 = (N + 255) / 256;
+    const long long pi = (long long)(cur.bh % n_layouts) * T2 + cur.t / 2;
+    const int e0 = min(max(sp_ptr[pi], 0), n_entries);
+    const int ne = min(min(max(sp_ptr[pi + 1], e0), n_entries) - e0, 128);
+    const int hbits = 24 + 4 * (cur.t & 1);
+    const unsigned ea = lane < ne ? sp_ent[e0 + lane] : 0u;
+    const unsigned eb = 64 + lane < ne ? sp_ent[e0 + 64 + lane] : 0u;
+    const bool va = ((ea >> hbits) & 0xFu) != 0u, vb = ((eb >> hbits) & 0xFu) != 0u;
+    const unsigned long long ba = __builtin_amdgcn_ballot_w64(va), bb = __builtin_amdgcn_ballot_w64(vb);
+    const int ca = __builtin_popcountll(ba);
+    cur.n_tiles = ca + __builtin_popcountll(bb);
+    const int pa = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(ba >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)ba, 0u));
+    const int pb = ca + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bb >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bb, 0u));
+    unsigned short* const lst = (unsigned short*)(lds_v + G::kTileV) + 128 * wave;
+    if (va) lst[pa] = (unsigned short)((ea & 0xFFu) | (((ea >> hbits) & 0xFu) << 8));
+    if (vb) lst[pb] = (unsigned short)((eb & 0xFFu) | (((eb >> hbits) & 0xFu) << 8));
+    sp_list = (unsigned)lst[lane] | ((unsigned)lst[64 + lane] << 16);
+    sp_bit = 8 + wave;
+    if (cur.n_tiles == 0) {
+      // no key for any row of the item: O = 0, LSE = -inf
+      constexpr int kEsz = OUT_BF16 ? 2 : 4;
+      const int qw0 = cur.t * kBr4 + 32 * wave;
+      const int rows = max(0, min(kRows, N - qw0));
+      const long long hd = (long long)cur.bh * N * D;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc((const char*)o + (hd + (long long)min(qw0, N) * D) * kEsz, rows * D * kEsz);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < kRows * D * kEsz / 1024; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(z, ro, u * 1024 + 16 * lane, 0, 0);
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (long long)cur.bh * N + min(qw0, N), rows * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), rl, l32 * 4, 0, 0);
+      return;
+    }
+  }
+  // entry of the item's sparse tile jt (uniform, 0 <= jt < n_tiles)
+  auto sp_entry = [&](int jt) __attribute__((always_inline)) {
+    return ((unsigned)__builtin_amdgcn_readlane((int)sp_list, jt & 63) >> (16 * (jt >> 6))) & 0xFFFFu;
+  };
+  // the current item's key tile of its tile jt (clamped to the last)
+  auto key_tile = [&](int jt) __attribute__((always_inline)) {
+    const int j = min(jt, cur.n_tiles - 1);
+    if constexpr (SPARSE) return min((int)(sp_entry(j) & 0xFFu), nk - 1);
+    else return cur.j_lo + j;
+  };
   // the current item's addresses and row bounds (set by enter())
   long long head = 0;
   const char* kh = nullptr;
@@ -1168,8 +1227,10 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // `slot`.  jt is clamped to the last tile (a copy past the end fetches it
   // again into a slot nobody reads); rows past N come from row N-1 and are
   // masked.
+  // (Block-sparse: the current item's tiles only; its items are not
+  // prefetched.)
   auto copy_k_of = [&](const char* kbase, int j_lo_, int n_tiles_, int jt, int slot, int kk) __attribute__((always_inline)) {
-    const int key0 = (j_lo_ + min(jt, n_tiles_ - 1)) * kBc;
+    const int key0 = (SPARSE ? key_tile(jt) : j_lo_ + min(jt, n_tiles_ - 1)) * kBc;
     const int rows = min(kBc, n_keys - key0);
     const unsigned long long gsrc = uniform_addr(kbase + (long long)key0 * G::kRowBytes);
     const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
@@ -1179,7 +1240,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     copy_k_of(kh, cur.j_lo, cur.n_tiles, jt, slot, kk);
   };
   auto copy_v = [&](int jt, int slot, int kk) __attribute__((always_inline)) {
-    const int key0 = (cur.j_lo + min(jt, cur.n_tiles - 1)) * kBc;
+    const int key0 = key_tile(jt) * kBc;
     const int rows = min(kBc, n_keys - key0);
     const unsigned long long gsrc = uniform_addr(vh + (long long)key0 * G::kRowBytes);
     const int lim = __builtin_amdgcn_readfirstlane((rows - 1) * G::kRowBytes + G::kRowBytes - 16);
@@ -1387,8 +1448,14 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // whole (window / causal edges, the ragged end of the sequence).  Element i
   // of block kb holds key 64*ja + 32*kb + 8*(i/4) + 4*half + (i%4).
   auto mask_tile = [&](int j, f32x16 (&sc)[2]) __attribute__((always_inline)) {
-    const int ja = cur.j_lo + j;
-    if (ja < cur.jf_lo || ja >= cur.jf_hi) {
+    const int ja = key_tile(j);
+    if (SPARSE && !((sp_entry(j) >> sp_bit) & 1u)) {
+      // block-sparse: this wavefront's rows see no key of the tile
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[kb][i] = -INFINITY;
+    } else if (ja < cur.jf_lo || ja >= cur.jf_hi) {
       const int key0 = ja * kBc;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -1702,7 +1769,23 @@ hipError_t launch_t(const FwdArgs& a) {
       auto kern = sc.sched == 0 ? fwd_kernel<D, MASKED, OUT_BF16, false> : fwd_kernel<D, MASKED, OUT_BF16, true>;
       hipLaunchKernelGGL(kern, dim3((unsigned)sc.workgroups), dim3(kThreads4), 0, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse, a.B * a.H, a.N, T4, c, a.poison ? 1 : 0,
-                         a.H / a.Hkv, a.wl, a.wr, (int)items, sc.sched);
+                         a.H / a.Hkv, a.wl, a.wr, (int)items, sc.sched, (const int*)nullptr,
+                         (const unsigned*)nullptr, 1, 0);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (SPARSE && !PAGED && !FP8) {
+    if (a.items == nullptr && a.N <= 64 * 128) {
+      // block-sparse with at most 128 key tiles per list: the 128-row
+      // kernel, one item per workgroup (an item streams only the key tiles
+      // its own rows see)
+      const int T4 = (a.N + kBr4 - 1) / kBr4;
+      const long long items = (long long)T4 * a.B * a.H;
+      if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((fwd_kernel<D, MASKED, OUT_BF16, false, true>), dim3((unsigned)items), dim3(kThreads4), 0,
+                         a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.o, a.lse,
+                         a.B * a.H, a.N, T4, c, a.poison ? 1 : 0, a.H / a.Hkv, a.wl, a.wr, (int)items, 0, a.sp_ptr,
+                         a.sp_ent, a.n_layouts, a.n_entries);
       return hipGetLastError();
     }
   }

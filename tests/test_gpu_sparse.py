@@ -56,6 +56,8 @@ CASES = [
     (1, 1, 1, 2049, 128, 512, 256, "one", 0.3, True, False, False),
     (2, 4, 2, 300, 64, 96, 64, "all", 0.6, False, False, True),
     (1, 2, 2, 1024, 128, 128, 64, "head", 0.15, False, False, False),
+    # past 8192 keys (more than 128 key tiles per list): the 256-row kernel
+    (1, 1, 1, 8300, 64, 128, 128, "one", 0.3, True, True, False),
 ]
 
 
