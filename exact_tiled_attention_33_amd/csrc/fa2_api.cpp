@@ -459,18 +459,21 @@ int fa2_decode_paged_workspace(int B, int H, int H_kv, int n_q, int d, int max_c
   if (split_keys < 0 || split_keys % bc != 0) return FA2_ERR_INVALID_ARG;
   if (split_keys == 0) {
     // At least four key tiles per chunk unless the context is shorter, and:
-    // - groups of up to 32 query rows run one wavefront per (chunk, group),
-    //   four per compute unit: enough chunks at the longest context for one
-    //   chunk per wavefront slot (more chunks start a second, partial round;
-    //   fewer leave slots idle), or four per sequence once the groups alone
-    //   fill the slots (smaller chunks balance the rounds);
+    // - groups of up to 128 query rows run one wavefront per (chunk, group,
+    //   block of 32 rows), four per compute unit: enough chunks at the
+    //   longest context for one chunk per wavefront slot (more chunks start
+    //   a second, partial round; fewer leave slots idle), or four per
+    //   sequence once the wavefronts of one chunk alone fill the slots
+    //   (smaller chunks balance the rounds);
     // - larger groups run workgroups of the forward kernel: about eight per
     //   compute unit at the longest context (about four on average for a
     //   mixed batch).
     if (num_units < 1) return FA2_ERR_INVALID_ARG;
     const long long groups = (long long)B * H_kv;
-    const long long slots = (long long)(H / H_kv) * n_q <= 32 ? 4LL * num_units : 0;
-    const long long want = slots > 0 ? (groups < slots ? (slots + groups - 1) / groups : 4)
+    const long long rows = (long long)(H / H_kv) * n_q;
+    const long long slots = rows <= 128 ? 4LL * num_units : 0;
+    const long long waves = groups * ((rows + 31) / 32);  // per chunk
+    const long long want = slots > 0 ? (waves < slots ? (slots + waves - 1) / waves : 4)
                                      : std::max<long long>(1, (8LL * num_units + groups - 1) / groups);
     long long keys = (max_context + want - 1) / want;
     keys = (keys + bc - 1) / bc * bc;

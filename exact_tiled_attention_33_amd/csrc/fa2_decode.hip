@@ -1,6 +1,7 @@
 // Decoding from a paged key/value cache with one wavefront per (chunk,
-// sequence, key/value head): the wavefront holds the group's query rows
-// (H/H_kv heads x n_q new tokens, at most 32) and streams the chunk's keys
+// sequence, key/value head, block of 32 query rows): the wavefront holds
+// 32 of the group's query rows (H/H_kv heads x n_q new tokens, at most 128
+// in all) and streams the chunk's keys
 // and values in 32-key tiles through its own double-buffered LDS ring, with
 // no workgroup barrier; four such wavefronts share a workgroup (and a CU)
 // and each keeps its next tile in flight.  Decoding reads every key and
@@ -151,9 +152,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_wave_kernel(const __bf1
   __shared__ __attribute__((aligned(1024))) char smem[kDecWaves * G::kWaveLds];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * kDecWaves + w;  // this wavefront's (chunk, group)
-  if (gw >= n_waves) return;                  // whole wavefronts only; no barrier in this kernel
-  const int g = gw % groups, chunk = gw / groups;
+  // this wavefront's (chunk, group, row block); the row blocks of a group
+  // are adjacent wavefronts, so a workgroup's wavefronts read the same pages
+  const int gw = blockIdx.x * kDecWaves + w;
+  if (gw >= n_waves) return;  // whole wavefronts only; no barrier in this kernel
+  const int n_rb = (nq_rows + 31) / 32, rb = gw % n_rb;
+  const int g = (gw / n_rb) % groups, chunk = gw / n_rb / groups;
   const int b = g / pg.kv_heads, kvh = g % pg.kv_heads;
   const int n_keys = min(min(max(pg.ctx_lens[b], 0), pg.max_pages * pg.page_size), max_keys);
   const int key_begin = chunk * pg.chunk_tiles * 64;
@@ -162,15 +166,16 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_wave_kernel(const __bf1
   const int t0 = key_begin / kDecKeys, nt = (key_end - key_begin + kDecKeys - 1) / kDecKeys;
   const int* const page_row = pg.page_table + (long long)b * pg.max_pages;
   const int l32 = lane & 31, half = lane >> 5;
-  const int qrow = l32;  // this lane's query row within the group
+  const int qrow = 32 * rb + l32;  // this lane's query row within the group
 
-  // Q rows of the group as MFMA B operands (query = lane % 32, dims
+  // The row block's Q rows as MFMA B operands (query = lane % 32, dims
   // 16*s + 8*half .. +7); rows past nq_rows read as zeros.
   bf16x8 qf[G::kKSteps];
   {
-    const __bf16* qg = q + (long long)g * nq_rows * D;
+    const __bf16* qg = q + ((long long)g * nq_rows + 32 * rb) * D;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>(qg), (short)0, __builtin_amdgcn_readfirstlane(nq_rows * D * 2), 0x00020000);
+        const_cast<__bf16*>(qg), (short)0, __builtin_amdgcn_readfirstlane(min(32, nq_rows - 32 * rb) * D * 2),
+        0x00020000);
 #pragma unroll
     for (int s = 0; s < G::kKSteps; ++s)
       qf[s] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -341,7 +346,7 @@ template <int D>
 hipError_t launch_wave_d(const FwdArgs& a) {
   const int groups = a.B * a.Hkv;
   const int nq_rows = (a.H / a.Hkv) * a.paged.n_q;
-  const long long n_waves = (long long)a.n_slots * groups;
+  const long long n_waves = (long long)a.n_slots * groups * ((nq_rows + 31) / 32);
   const long long grid = (n_waves + kDecWaves - 1) / kDecWaves;
   if (n_waves > 0x7fffffffLL || grid < 1) return hipErrorInvalidValue;
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);

@@ -1947,8 +1947,8 @@ hipError_t launch_paged_t(const FwdArgs& a) {
   if (grid > 0x7fffffffLL || grid < 1) return hipErrorInvalidValue;
   const float c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   hipError_t e;
-  if (nq_rows <= 32) {
-    // a group fits one wavefront: the lighter one-wavefront-per-chunk kernel
+  if (nq_rows <= 128) {
+    // up to four blocks of 32 rows: the lighter one-wavefront-per-chunk kernel
     e = launch_decode_waves(a);
   } else {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, false, false, false, true, false>), dim3((unsigned)grid), dim3(kThreads), 0,

@@ -412,12 +412,13 @@ int fa2_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* 
  *   B, H, H_kv, n_q, d, max_context   as for fa2_decode_paged.
  *   split_keys      keys per chunk (a multiple of 64), or 0: the library
  *                   picks the chunk from max_context, B*H_kv and num_units:
- *                   with (H/H_kv)*n_q <= 32, one chunk per wavefront slot
- *                   (four per unit) at the longest context, or four chunks
- *                   per sequence when B*H_kv alone fills the slots; with
- *                   larger groups about eight workgroups per unit at the
- *                   longest context; at least 256 keys per chunk unless the
- *                   context is shorter.
+ *                   with (H/H_kv)*n_q <= 128 (one wavefront per chunk and
+ *                   32 rows of a group), one chunk per wavefront slot (four
+ *                   per unit) at the longest context, or four chunks per
+ *                   sequence when one chunk's wavefronts alone fill the
+ *                   slots; with larger groups about eight workgroups per
+ *                   unit at the longest context; at least 256 keys per
+ *                   chunk unless the context is shorter.
  *   num_units       compute units of the device (used when split_keys == 0).
  *   split_keys_out, workspace_bytes  (host, non-NULL) receive the chunk
  *                   size and the workspace fa2_decode_paged needs for it.

@@ -16,10 +16,12 @@ def test_workspace_helper():
     assert fa2.fa2_decode_paged_workspace(16, 32, 8, 1, 128, 8192, 0, 256)[0] == 1024
     # the groups alone fill the slots: four chunks per sequence
     assert fa2.fa2_decode_paged_workspace(256, 32, 8, 1, 128, 8192, 0, 256)[0] == 2048
-    # groups of 64 rows (forward kernel workgroups): about eight per unit, at
+    # groups of 64 rows: two wavefronts (row blocks) per chunk and group; at
     # least 256 keys per chunk
     assert fa2.fa2_decode_paged_workspace(4, 64, 1, 1, 128, 8192, 0, 256)[0] == 256
-    assert fa2.fa2_decode_paged_workspace(1, 64, 1, 1, 128, 1 << 20, 0, 256)[0] == 512
+    assert fa2.fa2_decode_paged_workspace(1, 64, 1, 1, 128, 1 << 20, 0, 256)[0] == 2048
+    # groups of 256 rows (forward kernel workgroups): about eight per unit
+    assert fa2.fa2_decode_paged_workspace(1, 256, 1, 1, 128, 1 << 20, 0, 256)[0] == 512
     # a short context: one chunk covering it
     sk, ws = fa2.fa2_decode_paged_workspace(1, 8, 1, 1, 128, 100, 0, 256)
     assert sk == 128 and ws == 1 * 1 * 1 * 8 * (128 * 4 + 8)

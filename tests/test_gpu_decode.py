@@ -49,6 +49,11 @@ CASES = [
     # chunks of more than 64 pages: the page numbers are read 64 at a time
     (2, 8, 2, 1, 128, 64, [6000, 8191], 8192, False),
     (1, 4, 1, 2, 64, 64, [9000], 4160, False),
+    # groups of more than 32 rows: two, four and two (the second of one row)
+    # 32-row blocks per group
+    (2, 32, 2, 4, 128, 64, [700, 3000], 0, False),
+    (1, 16, 1, 8, 64, 64, [1500], 256, True),
+    (2, 33, 1, 1, 128, 128, [900, 64], 0, False),
     # many key/value heads: 32 of one row, 16 of two rows, 6 of two rows
     (1, 32, 32, 1, 128, 64, [100], 0, False),
     (2, 16, 16, 2, 64, 128, [300, 77], 64, True),
