@@ -1041,6 +1041,11 @@ struct KRing {
   static __device__ __forceinline__ int row_off(int r) { return (r % kSuper) * kSuperBytes + (r / kSuper) * kRowBytes; }
 };
 
+// Longest block-sparse list (key tiles of 64) the 128-row kernel takes: its
+// compacted entries keep the key tile in 12 bits, and the list costs
+// 2 bytes an entry of LDS (8 KiB, which two workgroups per CU still fit).
+constexpr int kSparseMaxTiles = 4096;
+
 template <int D, bool MASKED, bool OUT_BF16, bool PERSIST, bool SPARSE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads4, kThreads4), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -1056,7 +1061,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // K_{j+3} and V_{j+1}, which have two streams to arrive.
   constexpr int kR = D == 64 ? 3 : 2;
   using KR = KRing<D, kR>;
-  __shared__ __attribute__((aligned(1024))) char smem[KR::kBytes + kR * G::kTileV];
+  __shared__ __attribute__((aligned(1024))) char smem[KR::kBytes + kR * G::kTileV + (SPARSE ? 2 * kSparseMaxTiles : 0)];
   char* const lds_k = smem;
   char* const lds_v = smem + KR::kBytes;
 
@@ -1120,32 +1125,40 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   // tile's list (entry = key tile | slice bits << 24, bit s set when the
   // rows 32s .. 32s+31 of the 256-row tile see that key tile) whose four
   // slice bits of this 128-row half are not all clear, in the list's order.
-  // They are compacted once, through a scratch in V ring slot 1 (first
-  // written by a copy after the item's first barrier), into one lane
-  // register of 16-bit entries (key tile | the half's four slice bits << 8):
-  // entry i in bits 16*(i / 64) of lane i % 64.  At most 128 (the host takes
-  // this kernel only while N <= 8192, so key tiles fit 8 bits).
+  // They are compacted once, 256 list entries per round of loads, into an
+  // LDS array of 16-bit entries (key tile | the half's four slice bits << 12)
+  // that every wavefront writes whole: the same values at the same places,
+  // so each reads back its own writes without a barrier.  A lane register
+  // holds a window of 128 of them, entry sp_base + i in bits 16*(i / 64) of
+  // lane i % 64; lists longer than 128 move it on by 64 entries between
+  // tile pairs (a pair looks at most 4 entries past its first tile).
   unsigned sp_list = 0u;
-  int sp_bit = 0;  // this wavefront's slice bit in an entry
+  int sp_base = 0;  // the list entry in bits 0..15 of lane 0 of sp_list
+  int sp_bit = 0;   // this wavefront's slice bit in an entry
+  unsigned short* const sp_lst = (unsigned short*)(smem + KR::kBytes + kR * G::kTileV);
   if constexpr (SPARSE) {
     const int T2 = (N + 255) / 256;
     const long long pi = (long long)(cur.bh % n_layouts) * T2 + cur.t / 2;
     const int e0 = min(max(sp_ptr[pi], 0), n_entries);
-    const int ne = min(min(max(sp_ptr[pi + 1], e0), n_entries) - e0, 128);
+    const int ne = min(min(max(sp_ptr[pi + 1], e0), n_entries) - e0, kSparseMaxTiles);
     const int hbits = 24 + 4 * (cur.t & 1);
-    const unsigned ea = lane < ne ? sp_ent[e0 + lane] : 0u;
-    const unsigned eb = 64 + lane < ne ? sp_ent[e0 + 64 + lane] : 0u;
-    const bool va = ((ea >> hbits) & 0xFu) != 0u, vb = ((eb >> hbits) & 0xFu) != 0u;
-    const unsigned long long ba = __builtin_amdgcn_ballot_w64(va), bb = __builtin_amdgcn_ballot_w64(vb);
-    const int ca = __builtin_popcountll(ba);
-    cur.n_tiles = ca + __builtin_popcountll(bb);
-    const int pa = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(ba >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)ba, 0u));
-    const int pb = ca + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bb >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bb, 0u));
-    unsigned short* const lst = (unsigned short*)(lds_v + G::kTileV) + 128 * wave;
-    if (va) lst[pa] = (unsigned short)((ea & 0xFFu) | (((ea >> hbits) & 0xFu) << 8));
-    if (vb) lst[pb] = (unsigned short)((eb & 0xFFu) | (((eb >> hbits) & 0xFu) << 8));
-    sp_list = (unsigned)lst[lane] | ((unsigned)lst[64 + lane] << 16);
-    sp_bit = 8 + wave;
+    int cnt = 0;
+    for (int c0 = 0; c0 < ne; c0 += 256) {
+      unsigned e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = c0 + 64 * u + lane < ne ? sp_ent[e0 + c0 + 64 * u + lane] : 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool vis = ((e[u] >> hbits) & 0xFu) != 0u;
+        const unsigned long long b = __builtin_amdgcn_ballot_w64(vis);
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(b >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)b, 0u));
+        if (vis) sp_lst[pos] = (unsigned short)((e[u] & 0xFFFu) | (((e[u] >> hbits) & 0xFu) << 12));
+        cnt += __builtin_popcountll(b);
+      }
+    }
+    cur.n_tiles = cnt;
+    sp_list = (unsigned)sp_lst[lane] | ((unsigned)sp_lst[64 + lane] << 16);
+    sp_bit = 12 + wave;
     if (cur.n_tiles == 0) {
       // no key for any row of the item: O = 0, LSE = -inf
       constexpr int kEsz = OUT_BF16 ? 2 : 4;
@@ -1162,14 +1175,26 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
       return;
     }
   }
-  // entry of the item's sparse tile jt (uniform, 0 <= jt < n_tiles)
+  // entry of the item's sparse tile jt (uniform, sp_base <= jt < sp_base + 128)
   auto sp_entry = [&](int jt) __attribute__((always_inline)) {
-    return ((unsigned)__builtin_amdgcn_readlane((int)sp_list, jt & 63) >> (16 * (jt >> 6))) & 0xFFFFu;
+    const int i = jt - sp_base;
+    return ((unsigned)__builtin_amdgcn_readlane((int)sp_list, i & 63) >> (16 * ((i >> 6) & 1))) & 0xFFFFu;
+  };
+  // before the tile pair starting at tile j: a list longer than the window
+  // moves it on once j is 64 entries in
+  auto sp_window = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      if (cur.n_tiles > sp_base + 128 && j >= sp_base + 64) {
+        sp_base += 64;
+        sp_list = (unsigned)sp_lst[min(sp_base + lane, kSparseMaxTiles - 1)] |
+                  ((unsigned)sp_lst[min(sp_base + 64 + lane, kSparseMaxTiles - 1)] << 16);
+      }
+    }
   };
   // the current item's key tile of its tile jt (clamped to the last)
   auto key_tile = [&](int jt) __attribute__((always_inline)) {
     const int j = min(jt, cur.n_tiles - 1);
-    if constexpr (SPARSE) return min((int)(sp_entry(j) & 0xFFu), nk - 1);
+    if constexpr (SPARSE) return min((int)(sp_entry(j) & 0xFFFu), nk - 1);
     else return cur.j_lo + j;
   };
   // the current item's addresses and row bounds (set by enter())
@@ -1209,7 +1234,6 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
   int voff_k[kCopyK], voff_v[kCopyV];
 #pragma unroll
   for (int kk = 0; kk < kCopyK; ++kk) {
-    const int u = (wave + kk * kW4) * 64 + lane;
     // instruction wave + 4 kk: rows (wave + 4 kk) + kSuper * (lane / chunks)
     const int row = (wave + kk * kW4) + KR::kSuper * (lane / G::kChunks);
     voff_k[kk] = row * G::kRowBytes + (lane % G::kChunks) * 16;
@@ -1621,6 +1645,7 @@ void fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, cons
     tile(0, S0{}, F_{}, T_{}, CKV{});
     int j = 1;
     for (; j + 1 < cur.n_tiles; j += 2) {
+      sp_window(j);
       tile(j, S1{}, T_{}, T_{}, CKV{});
       tile(j + 1, S0{}, T_{}, T_{}, CKV{});
     }
@@ -1775,10 +1800,10 @@ hipError_t launch_t(const FwdArgs& a) {
     }
   }
   if constexpr (SPARSE && !PAGED && !FP8) {
-    if (a.items == nullptr && a.N <= 64 * 128) {
-      // block-sparse with at most 128 key tiles per list: the 128-row
-      // kernel, one item per workgroup (an item streams only the key tiles
-      // its own rows see)
+    if (a.items == nullptr && a.N <= 64 * kSparseMaxTiles) {
+      // block-sparse with at most kSparseMaxTiles key tiles per list: the
+      // 128-row kernel, one item per workgroup (an item streams only the key
+      // tiles its own rows see)
       const int T4 = (a.N + kBr4 - 1) / kBr4;
       const long long items = (long long)T4 * a.B * a.H;
       if (items > 0x7fffffffLL) return hipErrorInvalidValue;

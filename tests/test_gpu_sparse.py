@@ -56,8 +56,12 @@ CASES = [
     (1, 1, 1, 2049, 128, 512, 256, "one", 0.3, True, False, False),
     (2, 4, 2, 300, 64, 96, 64, "all", 0.6, False, False, True),
     (1, 2, 2, 1024, 128, 128, 64, "head", 0.15, False, False, False),
-    # past 8192 keys (more than 128 key tiles per list): the 256-row kernel
+    # past 8192 keys: lists longer than the 128-entry register window, which
+    # moves on by 64 entries (once, twice), and key tiles past 255
     (1, 1, 1, 8300, 64, 128, 128, "one", 0.3, True, True, False),
+    (1, 1, 1, 9000, 64, 256, 64, "one", 1.0, False, False, False),
+    (1, 1, 1, 10000, 128, 256, 128, "one", 1.0, True, False, True),
+    (1, 1, 1, 17000, 64, 128, 64, "one", 0.9, True, True, False),
 ]
 
 
@@ -159,4 +163,37 @@ def test_sparse_headline_size_sampled_rows():
         err_o = float(np.max(np.abs(_np64(o[b, h][rows]) - eo)))
         err_l = float(np.max(np.abs(_np64(lse[b, h][rows]) - el)))
         print(f"[sparse] head ({b},{h}): max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+        assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+def test_sparse_long_lists_sampled_rows():
+    """40,000 keys at d = 128 (625 key tiles; lists of up to ~470 entries, so
+    the register window moves on several times within an item), two heads
+    with their own masks of 128x128 blocks at density 0.75, causal: sampled
+    rows, among them the first and last of 128-row halves deep in the
+    sequence, against the oracle's definition."""
+    N, H, bq, bk, dens = 40000, 2, 128, 128, 0.75
+    q, k, v = (t.to(DEV) for t in _inputs(1, H, H, N, 128, seed=41, outliers=True))
+    print(f"[case] sparse 1x{H}x{N}x128 blocks {bq}x{bk} p={dens} causal, sampled rows", flush=True)
+    nb = -(-N // bq)
+    bm = workloads.make_block_mask(H, nb, -(-N // bk), dens, seed=42)
+    plan = fa2.fa2_sparse_plan(N, bq, bk, bm, True)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = fa2.forward_sparse(q, k, v, plan, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    rows = np.array(sorted({0, 31, 32, 127, 128, 20000 - 1, 20000, 32767, 32768, N - 129, N - 128, N - 1,
+                            *rng.integers(0, N, size=24).tolist()}))
+    for h in range(H):
+        Q, K, V = _np64(q[0, h]), _np64(k[0, h]), _np64(v[0, h])
+        s = ref.scores(Q[rows], K, scale)
+        vis = ref.visible_block_sparse(rows, np.arange(N), bm[h], bq, bk, True)
+        m, l, num = ref.softmax_stats(s, vis, V)
+        eo, el = ref.finalize(m, l, num)
+        ob, lb = _np64(o[0, h][rows]), _np64(lse[0, h][rows])
+        empty = np.isneginf(el)
+        assert np.array_equal(np.isneginf(lb), empty) and np.all(ob[empty] == 0.0)
+        err_o = float(np.max(np.abs(ob - eo)))
+        err_l = float(np.max(np.abs(lb[~empty] - el[~empty]))) if (~empty).any() else 0.0
+        print(f"[sparse] head {h}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
         assert err_o <= 1e-2 and err_l <= 1e-3
