@@ -197,3 +197,33 @@ def test_sparse_long_lists_sampled_rows():
         err_l = float(np.max(np.abs(lb[~empty] - el[~empty]))) if (~empty).any() else 0.0
         print(f"[sparse] head {h}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
         assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+@pytest.mark.parametrize("N", [262144, 262145])
+def test_sparse_length_limit_sampled_rows(N):
+    """At the 128-row kernel's limit of 4,096 key tiles (262,144 keys: key
+    tile 4,095 is the largest its 12-bit entries hold) and one key past it
+    (the 256-row kernel): one head, d = 64, a mask of 256x64 blocks at
+    density 0.1, not causal (lists of ~410 entries), sampled rows against
+    the oracle's definition."""
+    bq, bk, dens = 256, 64, 0.1
+    q, k, v = (t.to(DEV) for t in _inputs(1, 1, 1, N, 64, seed=43))
+    print(f"[case] sparse 1x1x{N}x64 blocks {bq}x{bk} p={dens}, sampled rows", flush=True)
+    bm = workloads.make_block_mask(1, -(-N // bq), -(-N // bk), dens, seed=44, keep_diagonal=False)
+    plan = fa2.fa2_sparse_plan(N, bq, bk, bm, False)
+    o, lse = fa2.forward_sparse(q, k, v, plan, scale=0.125)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(19)
+    rows = np.array(sorted({0, 127, 128, 255, 256, N - 257, N - 129, N - 128, N - 1,
+                            *rng.integers(0, N, size=20).tolist()}))
+    Q, K, V = _np64(q[0, 0]), _np64(k[0, 0]), _np64(v[0, 0])
+    s = ref.scores(Q[rows], K, 0.125)
+    vis = ref.visible_block_sparse(rows, np.arange(N), bm[0], bq, bk, False)
+    assert vis[:, -64:].any(), "no sampled row sees the last key tile"
+    m, l, num = ref.softmax_stats(s, vis, V)
+    eo, el = ref.finalize(m, l, num)
+    ob, lb = _np64(o[0, 0][rows]), _np64(lse[0, 0][rows])
+    err_o = float(np.max(np.abs(ob - eo)))
+    err_l = float(np.max(np.abs(lb - el)))
+    print(f"[sparse] N={N}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+    assert err_o <= 1e-2 and err_l <= 1e-3
