@@ -227,3 +227,32 @@ def test_sparse_length_limit_sampled_rows(N):
     err_l = float(np.max(np.abs(lb - el)))
     print(f"[sparse] N={N}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
     assert err_o <= 1e-2 and err_l <= 1e-3
+
+
+SPARSE_POISON = [(1000, 128, 128, 64, 0.5, True), (9000, 64, 256, 64, 1.0, False), (10000, 128, 256, 128, 1.0, True)]
+
+
+@pytest.mark.parametrize("N,d,bq,bk,dens,causal", SPARSE_POISON,
+                         ids=[f"{n}x{d}-b{bq}x{bk}-p{p}{'-causal' if c else ''}" for n, d, bq, bk, p, c in SPARSE_POISON])
+def test_sparse_lds_poison(monkeypatch, N, d, bq, bk, dens, causal):
+    """With FA2_DEBUG_POISON the kernel fills each K/V ring slot with NaN
+    before a tile is copied into it: a read ahead of a copy, a copy over a
+    slot still being read, or a list entry kept where the ring lives would
+    change O.  The result must be bitwise that of the ordinary run (lists
+    of up to 157 entries, so the window moves on)."""
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 2, N, d, seed=45, outliers=True))
+    print(f"[case] sparse poisoned LDS 1x2x{N}x{d} blocks {bq}x{bk} p={dens} causal={causal}", flush=True)
+    bm = workloads.make_block_mask(2, -(-N // bq), -(-N // bk), dens, seed=46, keep_diagonal=False)
+    plan = fa2.fa2_sparse_plan(N, bq, bk, bm, causal)
+    o0, l0 = fa2.forward_sparse(q, k, v, plan, scale=0.1)
+    monkeypatch.setenv("FA2_DEBUG_POISON", "1")
+    o1, l1 = fa2.forward_sparse(q, k, v, plan, scale=0.1)
+    monkeypatch.delenv("FA2_DEBUG_POISON")
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    if N <= 1000:
+        eo, el = ref.attention_ref_block_sparse(_np64(q), _np64(k), _np64(v), 0.1, bm, bq, bk, causal)
+        empty = np.isneginf(el)
+        assert np.array_equal(np.isneginf(_np64(l1)), empty)
+        assert float(np.max(np.abs(_np64(o1) - eo))) <= 1e-2
+        assert float(np.max(np.abs(_np64(l1)[~empty] - el[~empty]))) <= 1e-3
