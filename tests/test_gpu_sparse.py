@@ -10,7 +10,10 @@ others do not), causal or not, one mask for all heads, one per head or one
 per (sequence, head), with ragged lengths, d = 64 and 128, grouped
 key/value heads and bf16 O.  An all-ones mask must give what fa2_fwd gives
 to rounding (fa2_fwd runs another kernel, whose exponent arguments and sums
-round in another order) and match the oracle, bitwise run to run.
+round in another order) and match the oracle, bitwise run to run.  Lists
+longer than the kernel's 128-entry register window, sequences up to its
+limit of 262,144 keys and one key past it (sampled rows), and LDS-poison
+runs (bitwise equal to the ordinary ones) cover the entry window.
 """
 
 from __future__ import annotations
