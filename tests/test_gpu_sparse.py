@@ -65,6 +65,9 @@ CASES = [
     (1, 1, 1, 9000, 64, 256, 64, "one", 1.0, False, False, False),
     (1, 1, 1, 10000, 128, 256, 128, "one", 1.0, True, False, True),
     (1, 1, 1, 17000, 64, 128, 64, "one", 0.9, True, True, False),
+    # long lists with grouped key/value heads, one mask per head or per (b, h)
+    (1, 4, 2, 9000, 128, 128, 64, "head", 0.95, True, True, True),
+    (2, 2, 1, 8500, 64, 64, 128, "all", 0.8, False, False, False),
 ]
 
 
